@@ -1,0 +1,373 @@
+"""Plain CPU oracle of the routed Mixture-of-Experts layer forward pass.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check of the package entry file and the
+bench's cpu_baseline leg may import or call this module. The HIP path never does, and this
+module imports nothing from it: the two share no code, headers, tables or helpers. The
+only thing both consume is the seeded input generators in `workloads`.
+
+Sources (cited by page title and section in every function below):
+  [OC3]  "Как устроен Olmo-core 3: обучение больших MoE-моделей" -- the authority for what
+         the layer computes. Sections used: "Как задаётся конфигурация MoE" (config and
+         parameter counts), "Латентная проекция экспертов" (latent projection),
+         "Маршрутизация: как роутер выбирает экспертов" (routing), "Разрешение равенства
+         логитов и квантизация" (tie intent), "Балансировка нагрузки и вспомогательные
+         штрафы" (token counts), "Пересылка токенов между экспертами" (permutation),
+         "Вычисления экспертов и точность" (grouped experts, bf16 output), "SwiGLU с
+         квантизацией" (up/gate split, gate*sigmoid(gate)).
+  [TSM]  "Architecting Trillion-Scale Sparse Multimodal Models: Design and Training
+         Practices", section 1 -- the 896-expert latent scale (context only).
+
+Arithmetic. Every floating-point step runs in float64 and is rounded only where the pages
+fix a precision (router logits and scores in fp32; expert output in bf16; the restored
+output cast to the up-projection's dtype) or where the layer's storage dtype fixes one (the
+latent input z and the SwiGLU activation are stored in the layer dtype). bf16 rounding is
+round-to-nearest-even of the float64 value, done with frexp so the arithmetic is exact.
+
+Readings where the pages are silent (each is listed with its reason in the design notes):
+  * top-k order: key descending, ties to the lower expert index, -0.0 == +0.0, NaN keys
+    after every number (ties among NaNs by index);
+  * the permutation is a stable sort of the flat assignment index t*k+j by expert;
+  * the combine is o[t] = sum_j w[t,j] * Y[t,j], summed in j order, no extra normalisation;
+  * latent restore order: combine, then RMSNorm(eps, weight g, no bias), cast, up-projection;
+  * down/up projections carry no bias; all weights are stored (out_features, in_features).
+
+Pins (tests/test_oracle_pins.py): parameter counts against the element counts of the
+generated tensors and the golden table; logits against an exactly-rounded fsum dot
+product; gating against torch's softmax/sigmoid; selection against brute force over all
+k-subsets and against Python's sort; weights against closed forms (golden fixtures);
+histogram/permutation against invariants and a brute-force counting sort; the expert path
+against a dense evaluation of every expert on every token; special cases against torch's
+silu / rms_norm; permutation equivariance and RMSNorm scale invariance.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, fields
+from typing import Optional
+
+import numpy as np
+
+GATINGS = ("softmax", "topk_softmax", "sigmoid")
+DTYPES = ("f32", "bf16")
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    """Layer fields. [OC3 "Как задаётся конфигурация MoE"]: num_experts defaults to 1 and
+    hidden_size to 256; d_model, num_experts and top_k are set on the router config.
+    [OC3 "Маршрутизация"]: gating function, sigmoid_stability_epsilon, normalisation order,
+    restore_weight_scale, expert_weight_scale, original_top_k. [OC3 "Латентная проекция
+    экспертов"]: latent_dim and the up-projection input norm (bias-free RMSNorm default)."""
+    d_model: int
+    num_experts: int = 1
+    top_k: int = 1
+    hidden_size: int = 256
+    gating_function: str = "softmax"
+    sigmoid_stability_epsilon: Optional[float] = None
+    normalize_expert_weights: Optional[float] = None
+    restore_weight_scale: bool = False
+    expert_weight_scale: Optional[float] = None
+    original_top_k: Optional[int] = None
+    router_bias: bool = False
+    latent_dim: Optional[int] = None
+    up_proj_input_norm: bool = True
+    up_proj_input_norm_eps: float = 1e-5
+    dtype: str = "bf16"
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "MoEConfig":
+        names = {f.name for f in fields(cls)}
+        return cls(**{k: v for k, v in d.items() if k in names})
+
+    @property
+    def expert_dim(self) -> int:
+        """Width of the routed payload: latent_dim with a latent projection, else d_model."""
+        return self.latent_dim if self.latent_dim else self.d_model
+
+
+# ----------------------------------------------------------------------------- rounding
+
+def round_f32(a) -> np.ndarray:
+    """Round to the nearest float32 (ties to even); returned as float64 holding that value."""
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_bf16(a) -> np.ndarray:
+    """Round to the nearest bfloat16 (8 significant bits, ties to even), as float64.
+
+    a = m * 2**e with 0.5 <= |m| < 1; m * 2**8 is exact in float64, np.round rounds half to
+    even, so the result is the correctly rounded bf16 value. Below 2**-126 (bf16's subnormal
+    range) the spacing is fixed at 2**-133. (Overflow never occurs in the layer's values.)
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    normal = np.ldexp(np.round(m * 256.0) / 256.0, e)
+    sub = np.ldexp(np.round(np.ldexp(a, 133)), -133)
+    return np.where(np.abs(a) < 2.0 ** -126, sub, normal)
+
+
+def round_to(a, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return round_f32(a)
+    if dtype == "bf16":
+        return round_bf16(a)
+    raise ValueError(dtype)
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------- router
+
+def router_logits(x, router_weight, router_bias=None) -> np.ndarray:
+    """[OC3 "Маршрутизация"]: the router input is cast to fp32 and a linear layer with an
+    (num_experts, d_model) weight gives the (tokens, num_experts) logits. [OC3 "Как задаётся
+    конфигурация MoE"]: the router has d_model*num_experts weights plus num_experts bias terms
+    when bias is on. The dot products are summed in float64 and rounded to fp32 once.
+    Eval mode: the training-only jitter of [OC3 "Jitter при обучении"] is a no-op."""
+    l = _f64(x) @ _f64(router_weight).T
+    if router_bias is not None:
+        l = l + _f64(router_bias)[None, :]
+    return round_f32(l)
+
+
+def gating_scores(cfg: MoEConfig, logits) -> np.ndarray:
+    """[OC3 "Маршрутизация"]: softmax and topk_softmax both score with a softmax of the logits
+    over the expert axis; sigmoid scores each expert independently and, when
+    sigmoid_stability_epsilon is set, adds it to every score. Computed in float64 and rounded
+    to fp32; the epsilon is then added as an fp32 addition."""
+    l = _f64(logits)
+    if cfg.gating_function in ("softmax", "topk_softmax"):
+        m = l.max(axis=-1, keepdims=True)
+        e = np.exp(l - m)
+        return round_f32(e / e.sum(axis=-1, keepdims=True))
+    if cfg.gating_function == "sigmoid":
+        with np.errstate(over="ignore"):
+            s = round_f32(1.0 / (1.0 + np.exp(-l)))
+        if cfg.sigmoid_stability_epsilon:
+            s = round_f32(s + round_f32(cfg.sigmoid_stability_epsilon))
+        return s
+    raise ValueError(cfg.gating_function)
+
+
+def selection_keys(cfg: MoEConfig, logits, scores, score_bias=None) -> np.ndarray:
+    """[OC3 "Маршрутизация"] and [OC3 "Счётчики и bias-корректировка"]: topk_softmax picks
+    experts by logits (+ score_bias); the other gatings pick by scores (+ score_bias). The
+    bias only steers selection. The addition is one fp32 add per element."""
+    base = _f64(logits if cfg.gating_function == "topk_softmax" else scores)
+    if score_bias is None:
+        return base
+    return round_f32(base + _f64(score_bias)[None, :])
+
+
+def select_topk(keys, k: int) -> np.ndarray:
+    """Indices of the k largest keys per row, largest first.
+
+    [OC3 "Маршрутизация"] selects with topk (max when k == 1). The page's disabled tie
+    branch ([OC3 "Разрешение равенства логитов и квантизация"]) states the intent that equal
+    keys go to the lower expert index; that is the rule here. Keys compare as IEEE numbers
+    (-0.0 equals +0.0); NaN keys rank after every number, NaNs among themselves by index.
+    Implemented as a lexicographic sort on (is_nan, -key, expert index).
+    """
+    keys = _f64(keys)
+    T, E = keys.shape
+    nan = np.isnan(keys)
+    neg = np.where(nan, 0.0, -keys)
+    neg = np.where(neg == 0.0, 0.0, neg)  # one zero: -0.0 and +0.0 are the same key
+    eidx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((eidx, neg, nan), axis=-1)
+    return order[:, :k].astype(np.int64)
+
+
+def expert_weights(cfg: MoEConfig, logits, scores, idx) -> np.ndarray:
+    """[OC3 "Маршрутизация"]: topk_softmax weights are a softmax over the selected experts'
+    logits (bias not included); otherwise the weights are the original scores gathered at the
+    selected experts. Then, in this order: divide by the p-norm over the k weights when
+    normalize_expert_weights = p is set; multiply by top_k when restore_weight_scale; by
+    expert_weight_scale when set; by sqrt(original_top_k / top_k) when original_top_k differs
+    from top_k. float64, rounded to fp32 at the end."""
+    T = idx.shape[0]
+    k = cfg.top_k
+    rows = np.arange(T)[:, None]
+    if cfg.gating_function == "topk_softmax":
+        sel = _f64(logits)[rows, idx]
+        m = sel.max(axis=-1, keepdims=True)
+        e = np.exp(sel - m)
+        w = e / e.sum(axis=-1, keepdims=True)
+    else:
+        w = _f64(scores)[rows, idx]
+    p = cfg.normalize_expert_weights
+    if p:
+        w = w / (np.abs(w) ** p).sum(axis=-1, keepdims=True) ** (1.0 / p)
+    if cfg.restore_weight_scale:
+        w = w * k
+    if cfg.expert_weight_scale:
+        w = w * cfg.expert_weight_scale
+    if cfg.original_top_k and cfg.original_top_k != k:
+        w = w * (cfg.original_top_k / k) ** 0.5
+    return round_f32(w)
+
+
+def route(cfg: MoEConfig, logits, score_bias=None) -> dict:
+    """Gating, selection and weights from the logits ([OC3 "Маршрутизация"])."""
+    scores = gating_scores(cfg, logits)
+    keys = selection_keys(cfg, logits, scores, score_bias)
+    idx = select_topk(keys, cfg.top_k)
+    w = expert_weights(cfg, logits, scores, idx)
+    return dict(logits=_f64(logits), scores=scores, keys=keys, idx=idx, w=w)
+
+
+def route_from_scores(cfg: MoEConfig, sel_input, score_bias=None) -> dict:
+    """Selection and weights given the gating output: the scores for softmax/sigmoid, the
+    logits for topk_softmax (the input topk_softmax selects on). Same steps as route()."""
+    if cfg.gating_function == "topk_softmax":
+        logits, scores = sel_input, None
+    else:
+        logits, scores = None, sel_input
+    keys = selection_keys(cfg, logits, scores, score_bias)
+    idx = select_topk(keys, cfg.top_k)
+    w = expert_weights(cfg, logits, scores, idx)
+    return dict(keys=keys, idx=idx, w=w)
+
+
+# ----------------------------------------------------------------------- dispatch
+
+def expert_counts(idx, num_experts: int) -> np.ndarray:
+    """[OC3 "Балансировка нагрузки и вспомогательные штрафы"]: a histogram of the selected
+    indices summed over all tokens -- one count per expert."""
+    return np.bincount(np.asarray(idx).ravel(), minlength=num_experts).astype(np.int64)
+
+
+def expert_offsets(counts) -> np.ndarray:
+    """[OC3 "Пересылка токенов между экспертами"]: bins are the cumulative sum of the
+    per-expert counts; [OC3 "Вычисления экспертов и точность"]: offsets are int32 cumsums.
+    Returned with a leading 0 (length E+1)."""
+    return np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
+
+
+def stable_permutation(idx):
+    """[OC3 "Пересылка токенов между экспертами"]: sorting the expert indices orders the
+    assignments by expert. Read as a stable sort of the flat assignment index a = t*k + j by
+    expert, so inside one expert the assignments keep token order. Returns (perm, inv) with
+    perm[p] = the assignment at sorted position p and inv[perm[p]] = p."""
+    flat = np.asarray(idx).ravel()
+    perm = np.argsort(flat, kind="stable").astype(np.int64)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(flat.size)
+    return perm, inv
+
+
+# ---------------------------------------------------------------------- experts
+
+def prepare_routed_input(cfg: MoEConfig, x, down_proj=None) -> np.ndarray:
+    """[OC3 "Латентная проекция экспертов"]: without a latent projection the experts get the
+    input unchanged; with one, a down-projection maps (*, d_model) to (*, latent_dim). The
+    result is stored in the layer dtype."""
+    if not cfg.latent_dim:
+        return _f64(x)
+    return round_to(_f64(x) @ _f64(down_proj).T, cfg.dtype)
+
+
+def expert_mlp(cfg: MoEConfig, z_rows, w1_e, w2_e) -> np.ndarray:
+    """One expert's SwiGLU MLP on its rows.
+
+    [OC3 "Как задаётся конфигурация MoE"]: up_factor is 2 for swiglu, so the first matrix
+    has 2*hidden_size output rows. [OC3 "SwiGLU с квантизацией"]: the last dimension is split
+    in halves, first `up` then `gate`, and the activation is up * gate * sigmoid(gate) in
+    fp32 precision or better (float64 here), stored in the layer dtype. [OC3 "Вычисления
+    экспертов и точность"]: the grouped experts return bf16 (fp32 for an fp32 layer).
+    Weights are (2h, K) and (K, h), out x in."""
+    h = cfg.hidden_size
+    H = _f64(z_rows) @ _f64(w1_e).T
+    up, gate = H[:, :h], H[:, h:]
+    with np.errstate(over="ignore"):
+        act = round_to(up * gate / (1.0 + np.exp(-gate)), cfg.dtype)
+    return round_to(act @ _f64(w2_e).T, cfg.dtype)
+
+
+def run_experts(cfg: MoEConfig, z, idx, w1, w2) -> dict:
+    """[OC3 "Вычисления экспертов и точность"]: group the permuted tokens by expert, run each
+    expert's MLP, and return the results; Y is kept in sorted (permuted) order here.
+    w1/w2 may be arrays (E, ...) or mappings expert -> array (only touched experts needed)."""
+    k = cfg.top_k
+    counts = expert_counts(idx, cfg.num_experts)
+    offsets = expert_offsets(counts)
+    perm, inv = stable_permutation(idx)
+    z_perm = _f64(z)[perm // k]
+    Y = np.zeros((perm.size, _f64(z).shape[1]))
+    for e in np.nonzero(counts)[0]:
+        rows = slice(offsets[e], offsets[e + 1])
+        Y[rows] = expert_mlp(cfg, z_perm[rows], w1[e], w2[e])
+    return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, z_perm=z_perm, Y=Y)
+
+
+def combine(cfg: MoEConfig, Y, inv, w) -> np.ndarray:
+    """Unpermute and weight. [OC3 "Пересылка токенов между экспертами"]: results go back to
+    the original positions by a scatter with the saved indices. The router's weights have no
+    other consumer, so each token's k results are scaled by its weights and summed
+    (o[t] = sum_j w[t,j] * Y[inv[t*k+j]], j ascending)."""
+    k = cfg.top_k
+    w = _f64(w)
+    T = w.shape[0]
+    inv = np.asarray(inv).reshape(T, k)
+    o = np.zeros((T, Y.shape[1]))
+    for j in range(k):
+        o += w[:, j:j + 1] * Y[inv[:, j]]
+    return o
+
+
+def restore_routed_output(cfg: MoEConfig, o, norm_weight=None, up_proj=None) -> dict:
+    """[OC3 "Латентная проекция экспертов"]: without an up-projection the expert output is
+    returned as is; with one it is normalised (bias-free RMSNorm unless configured off),
+    cast to the up-projection weight's dtype and multiplied by it, giving (*, d_model).
+    [OC3 "Вычисления экспертов и точность"]: the cast before the dense up-projection.
+    RMSNorm: n = o / sqrt(mean(o**2) + eps) * g."""
+    o = _f64(o)
+    if not cfg.latent_dim:
+        return dict(n=None, y=o)
+    if cfg.up_proj_input_norm:
+        g = np.ones(o.shape[1]) if norm_weight is None else _f64(norm_weight)
+        n = o / np.sqrt((o * o).mean(axis=-1, keepdims=True) + cfg.up_proj_input_norm_eps) * g
+    else:
+        n = o
+    n = round_to(n, cfg.dtype)
+    return dict(n=n, y=n @ _f64(up_proj).T)
+
+
+def forward(cfg: MoEConfig, weights: dict, x) -> dict:
+    """The whole layer, step by step. `weights` holds numpy arrays (bf16 values as float32):
+    router_weight (E,d), router_bias (E)|None, score_bias (E)|None, down_proj (L,d)|None,
+    norm_weight (L)|None, up_proj (d,L)|None, w1 (E,2h,K) or {e: (2h,K)}, w2 (E,K,h) or
+    {e: (K,h)}. The final y is returned unrounded (float64)."""
+    out = {}
+    logits = router_logits(x, weights["router_weight"], weights.get("router_bias"))
+    out.update(route(cfg, logits, weights.get("score_bias")))
+    z = prepare_routed_input(cfg, x, weights.get("down_proj"))
+    out["z"] = z
+    out.update(run_experts(cfg, z, out["idx"], weights["w1"], weights["w2"]))
+    o = combine(cfg, out["Y"], out["inv"], out["w"])
+    out["o"] = o
+    out.update(restore_routed_output(cfg, o, weights.get("norm_weight"), weights.get("up_proj")))
+    return out
+
+
+# ------------------------------------------------------------------- parameter counts
+
+def num_params(cfg: MoEConfig) -> dict:
+    """[OC3 "Как задаётся конфигурация MoE"]: the latent dimension is d_model when there is no
+    latent MoE; total = router params + 3*latent_dim*hidden_size*num_experts (+ shared
+    modules, none here); active = total - 3*latent_dim*hidden_size*num_experts +
+    3*latent_dim*hidden_size*top_k. Router = d_model*num_experts (+num_experts with bias);
+    per expert (up_factor + 1)*dim*hidden_size with up_factor = 2 for swiglu, experts being
+    built with d_model = latent_dim. The latent projections and norm weight are not in the
+    page's formula; they are reported separately as `latent_extra`."""
+    L = cfg.latent_dim if cfg.latent_dim else cfg.d_model
+    router = cfg.d_model * cfg.num_experts + (cfg.num_experts if cfg.router_bias else 0)
+    up_factor = 2
+    experts = (up_factor + 1) * L * cfg.hidden_size * cfg.num_experts
+    total = router + experts
+    active = total - 3 * L * cfg.hidden_size * cfg.num_experts + 3 * L * cfg.hidden_size * cfg.top_k
+    extra = 0
+    if cfg.latent_dim:
+        extra = 2 * cfg.d_model * cfg.latent_dim + (cfg.latent_dim if cfg.up_proj_input_norm else 0)
+    return dict(total=total, active=active, latent_extra=extra)

@@ -1,0 +1,94 @@
+"""Planted mistakes in the CPU oracle must each fail at least one pin.
+
+Each case patches one oracle function with a plausible bug (swapped operand, dropped term,
+wrong index, wrong order of steps) and runs the pin that should catch it. CPU only; the
+patch lives only inside the test.
+"""
+import numpy as np
+import pytest
+
+import test_oracle_pins as P
+from oracle import moe_oracle as O
+
+
+def _swapped_up_gate(cfg, z_rows, w1_e, w2_e):
+    h = cfg.hidden_size
+    H = np.asarray(z_rows, np.float64) @ np.asarray(w1_e, np.float64).T
+    gate, up = H[:, :h], H[:, h:]  # halves swapped
+    act = O.round_to(up * gate / (1.0 + np.exp(-gate)), cfg.dtype)
+    return O.round_to(act @ np.asarray(w2_e, np.float64).T, cfg.dtype)
+
+
+def _ties_to_higher_index(keys, k):
+    keys = np.asarray(keys, np.float64)
+    T, E = keys.shape
+    nan = np.isnan(keys)
+    neg = np.where(nan, 0.0, -keys)
+    eidx = np.broadcast_to(-np.arange(E), (T, E))  # reversed tie rule
+    return np.lexsort((eidx, neg, nan), axis=-1)[:, :k]
+
+
+def _combine_with_perm(cfg, Y, inv, w):
+    k = cfg.top_k
+    w = np.asarray(w, np.float64)
+    T = w.shape[0]
+    perm = np.argsort(np.asarray(inv))  # uses perm where inv is needed
+    perm = perm.reshape(T, k)
+    o = np.zeros((T, Y.shape[1]))
+    for j in range(k):
+        o += w[:, j:j + 1] * Y[perm[:, j]]
+    return o
+
+
+_orig_weights = O.expert_weights
+
+
+def _weights_from_keys(cfg, logits, scores, idx):
+    # gathers the biased keys instead of the original scores
+    return _orig_weights(cfg, logits, None if scores is None else scores + 0.5, idx)
+
+
+def _scale_before_normalise(cfg, logits, scores, idx):
+    import dataclasses
+    c = dataclasses.replace(cfg, normalize_expert_weights=None)
+    w = _orig_weights(c, logits, scores, idx)
+    p = cfg.normalize_expert_weights
+    if p:
+        w = w / (np.abs(w) ** p).sum(-1, keepdims=True) ** (1.0 / p)
+    return w
+
+
+def _norm_without_mean(cfg, o, norm_weight=None, up_proj=None):
+    o = np.asarray(o, np.float64)
+    if not cfg.latent_dim:
+        return dict(n=None, y=o)
+    n = o / np.sqrt((o * o).sum(-1, keepdims=True) + cfg.up_proj_input_norm_eps)  # sum, not mean
+    n = O.round_to(n, cfg.dtype)
+    return dict(n=n, y=n @ np.asarray(up_proj, np.float64).T)
+
+
+def _golden(name):
+    return [c for c in P._golden_cases() if c["name"] == name][0]
+
+
+MUTATIONS = [
+    ("expert_mlp", _swapped_up_gate, lambda: P.test_single_expert_layer_is_plain_swiglu_mlp()),
+    ("select_topk", _ties_to_higher_index,
+     lambda: P.test_select_topk_brute_force_all_subsets(6)),
+    ("combine", _combine_with_perm, lambda: P.test_dense_bruteforce_equals_permuted_path(
+        "tiny_f32", dict(d_model=64, num_experts=6, top_k=3, hidden_size=32), 1e-6)),
+    ("expert_weights", _weights_from_keys,
+     lambda: P.test_routing_closed_forms(_golden("softmax_ln_ratios"))),
+    ("expert_weights", _scale_before_normalise,
+     lambda: P.test_routing_closed_forms(_golden("softmax_restore_scale"))),
+    ("restore_routed_output", _norm_without_mean,
+     lambda: P.test_identity_latent_reduces_to_rmsnorm_of_plain_layer()),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, target, bad, pin):
+    monkeypatch.setattr(O, target, bad)
+    with pytest.raises(AssertionError):
+        pin()

@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a closed form derived from the page
+"Как устроен Olmo-core 3: обучение больших MoE-моделей" (golden fixtures under
+tests/golden/), a library routine (torch's softmax / sigmoid / silu / rms_norm / bf16 cast,
+Python's sort, math.fsum), brute force over all subsets, or an invariant of the method.
+CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def cfg_of(**kw):
+    base = dict(d_model=64, num_experts=4, top_k=2, hidden_size=32, dtype="f32")
+    base.update(kw)
+    return O.MoEConfig(**base)
+
+
+def small_workload(name, T, **over):
+    cfg, w, x = workloads.make_workload(name, tokens=T, device="cpu", **over)
+    wn = {k: workloads.to_numpy_f32(v) for k, v in w.items()}
+    return O.MoEConfig.from_dict(cfg), wn, workloads.to_numpy_f32(x)
+
+
+# ------------------------------------------------------------------ parameter counts
+
+def _golden_params():
+    rows = {}
+    with open(os.path.join(GOLDEN, "param_counts.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            p = line.split()
+            rows[p[0]] = tuple(int(v) for v in p[1:4])
+    return rows
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_param_counts_golden(name):
+    cfg = O.MoEConfig.from_dict(workloads.layer_config(name))
+    got = O.num_params(cfg)
+    assert (got["total"], got["active"], got["latent_extra"]) == _golden_params()[name]
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny_f32", {}),
+    ("olmoe", dict(d_model=128, hidden_size=64, num_experts=6, top_k=3)),
+    ("latent896", dict(d_model=128, latent_dim=64, hidden_size=32, num_experts=10, top_k=4)),
+])
+def test_param_counts_equal_generated_tensor_sizes(name, over):
+    """Count the elements of the tensors a layer actually holds: router weight plus every
+    expert's two matrices; active = router plus top_k experts' matrices."""
+    cfg, w, _ = workloads.make_workload(name, tokens=4, **over)
+    c = O.MoEConfig.from_dict(cfg)
+    per_expert = w["w1"][0].numel() + w["w2"][0].numel()
+    total = w["router_weight"].numel() + w["w1"].numel() + w["w2"].numel()
+    active = w["router_weight"].numel() + c.top_k * per_expert
+    got = O.num_params(c)
+    assert got["total"] == total and got["active"] == active
+    if c.latent_dim:
+        assert got["latent_extra"] == (w["down_proj"].numel() + w["up_proj"].numel()
+                                       + w["norm_weight"].numel())
+
+
+# ------------------------------------------------------------------ rounding and logits
+
+def test_round_bf16_matches_torch_cast():
+    g = np.random.default_rng(1)
+    a = np.concatenate([g.standard_normal(200000).astype(np.float32),
+                        g.standard_normal(1000).astype(np.float32) * 1e-30,
+                        g.standard_normal(1000).astype(np.float32) * 1e30])
+    # exact ties between two bf16 neighbours
+    ties = (g.integers(1 << 15, 1 << 16, 5000).astype(np.uint32) << 16) | 0x8000
+    a = np.concatenate([a, ties.view(np.float32)])
+    a = a[np.isfinite(a)]
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(a), ref)
+
+
+def test_logits_exactly_rounded_dot():
+    """fp32 x fp32 products are exact in float64; math.fsum returns the correctly rounded sum,
+    so round_f32(fsum) is the exactly rounded logit. The oracle's float64 BLAS sum may differ
+    only below float64 resolution: at most one fp32 ulp, and almost never."""
+    cfg, w, x = small_workload("tiny_f32", 16)
+    got = O.router_logits(x, w["router_weight"])
+    W = w["router_weight"].astype(np.float64)
+    ref = np.array([[np.float32(math.fsum(x[t].astype(np.float64) * W[e]))
+                     for e in range(W.shape[0])] for t in range(x.shape[0])], dtype=np.float64)
+    ulps = np.abs(got.astype(np.float32).view(np.int32) - ref.astype(np.float32).view(np.int32))
+    assert ulps.max() <= 1 and (ulps == 0).mean() > 0.99
+
+
+def test_logits_bias_added():
+    cfg, w, x = small_workload("tiny_f32", 8)
+    b = np.linspace(-1, 1, w["router_weight"].shape[0]).astype(np.float32)
+    d = O.router_logits(x, w["router_weight"], b) - O.router_logits(x, w["router_weight"])
+    assert np.allclose(d, b[None, :], atol=1e-5)
+
+
+# ------------------------------------------------------------------ gating
+
+def test_softmax_gating_matches_torch():
+    g = np.random.default_rng(2)
+    l = O.round_f32(g.standard_normal((64, 37)) * 3)
+    got = O.gating_scores(cfg_of(gating_function="softmax", num_experts=37), l)
+    ref = torch.softmax(torch.from_numpy(l), dim=-1).numpy()
+    assert np.allclose(got, ref, rtol=2 ** -23, atol=0)
+    assert np.allclose(got.sum(-1), 1.0, atol=37 * 2 ** -24)
+
+
+def test_sigmoid_gating_matches_torch_and_eps():
+    g = np.random.default_rng(3)
+    l = O.round_f32(g.standard_normal((64, 19)) * 8)
+    l[0, :3] = [-1e4, 1e4, 0.0]
+    s = O.gating_scores(cfg_of(gating_function="sigmoid", num_experts=19), l)
+    ref = torch.sigmoid(torch.from_numpy(l)).numpy()
+    assert np.allclose(s, ref, rtol=2 ** -23, atol=0)
+    se = O.gating_scores(cfg_of(gating_function="sigmoid", num_experts=19,
+                                sigmoid_stability_epsilon=1e-6), l)
+    eps32 = float(np.float32(1e-6))
+    assert np.array_equal(se, (s.astype(np.float32) + np.float32(eps32)).astype(np.float64))
+    assert se[0, 0] == np.float32(eps32)  # all-negative logit: score is exactly eps, not 0
+
+
+# ------------------------------------------------------------------ top-k selection
+
+def _valid_topk_set(keys, S):
+    """Characterisation of the top-k set: every selected key ranks above every unselected key
+    under (NaN last, larger first, lower index first at equal keys)."""
+    def rank_above(a, b):
+        ka, kb = keys[a], keys[b]
+        if math.isnan(ka) or math.isnan(kb):
+            if math.isnan(ka) and math.isnan(kb):
+                return a < b
+            return not math.isnan(ka)
+        if ka != kb:
+            return ka > kb
+        return a < b
+    return all(rank_above(a, b) for a in S for b in range(len(keys)) if b not in S)
+
+
+@pytest.mark.parametrize("E", [4, 5, 6, 7, 8])
+def test_select_topk_brute_force_all_subsets(E):
+    g = np.random.default_rng(E)
+    grid = np.array([-1.0, -0.5, -0.0, 0.0, 0.5, 1.0, np.nan])
+    for trial in range(60):
+        keys = g.choice(grid, size=E) if trial % 2 else g.standard_normal(E)
+        for k in range(1, E + 1):
+            valid = [set(S) for S in itertools.combinations(range(E), k)
+                     if _valid_topk_set(keys, set(S))]
+            assert len(valid) == 1
+            got = O.select_topk(keys[None, :], k)[0]
+            assert set(got.tolist()) == valid[0]
+            # within the row: non-increasing keys, index ascending among equal keys
+            order = sorted(range(E), key=lambda e: (math.isnan(keys[e]),
+                                                    0.0 if math.isnan(keys[e]) else -keys[e], e))
+            assert got.tolist() == order[:k]
+
+
+def test_select_topk_matches_python_sort_wide():
+    s = workloads.synthetic_scores(300, 64, "nan").numpy().astype(np.float64)
+    got = O.select_topk(s, 8)
+    for t in range(s.shape[0]):
+        row = s[t]
+        order = sorted(range(64), key=lambda e: (math.isnan(row[e]),
+                                                 0.0 if math.isnan(row[e]) else -row[e], e))
+        assert got[t].tolist() == order[:8]
+
+
+def test_signed_zero_ties_go_to_lower_index():
+    keys = np.array([[-0.0, 0.0, -1.0], [0.0, -0.0, -1.0]])
+    assert O.select_topk(keys, 1)[:, 0].tolist() == [0, 0]
+
+
+# ------------------------------------------------------------------ weights
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "routing_closed_forms.jsonl")) as f:
+        return [json.loads(line) for line in f if line.strip()]
+
+
+def _num(v):
+    if isinstance(v, str):
+        sign = -1.0 if v.startswith("-") else 1.0
+        return sign * math.log(float(v.lstrip("-")[2:]))
+    return float(v)
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_routing_closed_forms(case):
+    E = len(case["logits"])
+    cfg = cfg_of(num_experts=E, **case["cfg"])
+    logits = O.round_f32(np.array([[_num(v) for v in case["logits"]]]))
+    bias = None if case["bias"] is None else np.array(case["bias"], dtype=np.float32)
+    r = O.route(cfg, logits, bias)
+    assert r["idx"][0].tolist() == case["idx"]
+    assert np.allclose(r["w"][0], case["w"], rtol=case["tol"], atol=case["tol"])
+
+
+def test_weight_invariants():
+    s = workloads.synthetic_scores(500, 32, "normal").numpy()
+    l = O.round_f32(s * 2)
+    c1 = cfg_of(num_experts=32, top_k=6, gating_function="softmax", normalize_expert_weights=1.0)
+    w1 = O.route(c1, l)["w"]
+    assert np.all(np.abs(w1.sum(-1) - 1) <= 6 * 2 ** -23)
+    c2 = cfg_of(num_experts=32, top_k=6, gating_function="topk_softmax")
+    w2 = O.route(c2, l)["w"]
+    assert np.all(np.abs(w2.sum(-1) - 1) <= 6 * 2 ** -23)
+    c3 = cfg_of(num_experts=32, top_k=1, gating_function="topk_softmax")
+    assert np.all(O.route(c3, l)["w"] == 1.0)
+    c4 = cfg_of(num_experts=32, top_k=6, gating_function="softmax")
+    w4 = O.route(c4, l)["w"]
+    assert np.all((w4 > 0) & (w4 <= 1))
+    eps = 1e-6
+    c5 = cfg_of(num_experts=32, top_k=6, gating_function="sigmoid", sigmoid_stability_epsilon=eps)
+    w5 = O.route(c5, l * 50)["w"]
+    assert np.all((w5 >= np.float32(eps)) & (w5 <= 1 + eps))
+    # weights are non-increasing along j for gathered scores without bias
+    assert np.all(np.diff(w4, axis=-1) <= 0)
+
+
+def test_topk_softmax_with_all_experts_equals_softmax():
+    s = workloads.synthetic_scores(50, 12, "normal").numpy()
+    l = O.round_f32(s)
+    a = O.route(cfg_of(num_experts=12, top_k=12, gating_function="topk_softmax"), l)
+    b = O.route(cfg_of(num_experts=12, top_k=12, gating_function="softmax"), l)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.allclose(a["w"], b["w"], rtol=2 ** -22, atol=0)
+
+
+# ------------------------------------------------------------------ histogram / permutation
+
+def test_histogram_and_permutation_invariants():
+    T, E, k = 777, 50, 6
+    idx = workloads.random_distinct_indices(T, E, k, skew=1.2).numpy()
+    counts = O.expert_counts(idx, E)
+    offsets = O.expert_offsets(counts)
+    perm, inv = O.stable_permutation(idx)
+    A = T * k
+    assert counts.sum() == A and offsets[-1] == A and np.all(np.diff(offsets) >= 0)
+    assert sorted(perm.tolist()) == list(range(A))
+    assert np.array_equal(inv[perm], np.arange(A))
+    flat = idx.ravel()
+    assert np.all(np.diff(flat[perm]) >= 0)
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+    # brute-force counting sort: visit experts in order, assignments in order
+    brute = [a for e in range(E) for a in range(A) if flat[a] == e]
+    assert perm.tolist() == brute
+    for e in range(E):
+        assert counts[e] == sum(1 for a in range(A) if flat[a] == e)
+
+
+# ------------------------------------------------------------------ expert path
+
+def _torch_swiglu_mlp(z, w1e, w2e, h, rnd):
+    """Independent SwiGLU MLP: torch's silu, float64, rounding by torch's dtype casts."""
+    H = torch.from_numpy(np.asarray(z, np.float64)) @ torch.from_numpy(np.asarray(w1e, np.float64)).T
+    up, gate = H[:, :h], H[:, h:]
+    act = rnd(up * torch.nn.functional.silu(gate))
+    return rnd(act @ torch.from_numpy(np.asarray(w2e, np.float64)).T)
+
+
+def _torch_round(dtype):
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    return lambda t: t.to(td).to(torch.float64)
+
+
+@pytest.mark.parametrize("name,over,rtol", [
+    ("tiny_f32", dict(d_model=64, num_experts=6, top_k=3, hidden_size=32), 1e-6),
+    ("olmoe", dict(d_model=64, num_experts=7, top_k=3, hidden_size=64), 2e-2),
+    ("latent896", dict(d_model=128, latent_dim=64, num_experts=9, top_k=4, hidden_size=32), 2e-2),
+])
+def test_dense_bruteforce_equals_permuted_path(name, over, rtol):
+    """Evaluate every expert on every token (no permutation), weight and sum; compare with the
+    oracle's sort/group/scatter path. Pins the permutation, the unpermute and the combine."""
+    T = 41
+    cfg, w, x = small_workload(name, T, **over)
+    out = O.forward(cfg, w, x)
+    rnd = _torch_round(cfg.dtype)
+    z = out["z"]
+    K = z.shape[1]
+    every = np.stack([_torch_swiglu_mlp(z, w["w1"][e], w["w2"][e], cfg.hidden_size, rnd).numpy()
+                      for e in range(cfg.num_experts)])  # (E, T, K)
+    o = np.zeros((T, K))
+    for t in range(T):
+        for j in range(cfg.top_k):
+            o[t] += out["w"][t, j] * every[out["idx"][t, j], t]
+    scale = np.abs(o).max()
+    assert np.abs(o - out["o"]).max() <= rtol * scale
+
+
+def test_single_expert_layer_is_plain_swiglu_mlp():
+    cfg, w, x = small_workload("tiny_f32", 33, num_experts=1, top_k=1, d_model=64,
+                               hidden_size=48)
+    out = O.forward(cfg, w, x)
+    assert np.all(out["w"] == 1.0) and np.all(out["idx"] == 0)
+    ref = _torch_swiglu_mlp(x, w["w1"][0], w["w2"][0], 48, _torch_round("f32")).numpy()
+    assert np.allclose(out["y"], ref, rtol=1e-6, atol=1e-7)
+
+
+def test_all_experts_softmax_is_dense_soft_mixture():
+    E = 5
+    cfg, w, x = small_workload("tiny_f32", 29, num_experts=E, top_k=E, d_model=64,
+                               hidden_size=32)
+    out = O.forward(cfg, w, x)
+    s = torch.softmax(torch.from_numpy(O.router_logits(x, w["router_weight"])), -1)
+    s = s.to(torch.float32).to(torch.float64).numpy()
+    ref = sum(s[:, e:e + 1] * _torch_swiglu_mlp(x, w["w1"][e], w["w2"][e], 32,
+                                                 _torch_round("f32")).numpy() for e in range(E))
+    assert np.allclose(out["y"], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_identity_latent_reduces_to_rmsnorm_of_plain_layer():
+    d = 64
+    cfg, w, x = small_workload("latent896", 21, d_model=d, latent_dim=d, num_experts=6, top_k=2,
+                               hidden_size=32, dtype="f32")
+    w["down_proj"] = np.eye(d, dtype=np.float32)
+    w["up_proj"] = np.eye(d, dtype=np.float32)
+    lat = O.forward(cfg, w, x)
+    plain_cfg = O.MoEConfig(**{**cfg.__dict__, "latent_dim": None})
+    plain = O.forward(plain_cfg, w, x)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(plain["y"]), (d,),
+                                       eps=cfg.up_proj_input_norm_eps).to(torch.float32)
+    assert np.allclose(lat["y"], ref.to(torch.float64).numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_rmsnorm_scale_invariance():
+    """Scaling the weights scales o; RMSNorm removes the scale exactly when eps is negligible
+    against mean(o^2): fan-in init (o of order 0.1-1) and eps = 1e-12 here."""
+    cfg, w, x = small_workload("tiny_f32", 25, d_model=128, latent_dim=64, num_experts=8,
+                               top_k=3, hidden_size=32, up_proj_input_norm_eps=1e-12)
+    a = O.forward(cfg, w, x)
+    assert (a["o"] ** 2).mean(-1).min() > 1e3 * cfg.up_proj_input_norm_eps
+    scaled = O.MoEConfig(**{**cfg.__dict__, "expert_weight_scale": 3.0})
+    b = O.forward(scaled, w, x)
+    assert np.allclose(a["y"], b["y"], rtol=1e-6, atol=1e-6)
+    assert np.allclose(b["w"], 3 * a["w"], rtol=1e-6)
+
+
+def test_token_permutation_equivariance():
+    cfg, w, x = small_workload("olmoe", 50, d_model=64, num_experts=8, top_k=2, hidden_size=32,
+                               dtype="f32")
+    p = np.random.default_rng(5).permutation(50)
+    a = O.forward(cfg, w, x)
+    b = O.forward(cfg, w, x[p])
+    assert np.array_equal(a["idx"][p], b["idx"])
+    assert np.allclose(a["y"][p], b["y"], rtol=1e-6, atol=1e-7)
+
+
+def test_counts_feed_offsets_and_perm_on_full_layer():
+    cfg, w, x = small_workload("latent896", 64, d_model=128, latent_dim=64, num_experts=16,
+                               top_k=4, hidden_size=32)
+    out = O.forward(cfg, w, x)
+    assert out["counts"].sum() == 64 * 4
+    for t in range(64):
+        assert len(set(out["idx"][t].tolist())) == 4
