@@ -1,0 +1,159 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE layer forward on one MI355X.
+
+A step is one full forward of the layer (router -> gating/top-k -> dispatch -> [latent down]
+-> grouped SwiGLU experts -> combine [-> norm -> latent up]) over one batch of synthetic
+tokens, with inputs and weights resident in HBM. Default workload: the OlmoE-shaped layer
+(8192 tokens, d_model 2048, 64 experts, top-8, hidden 1024, bf16, fp32 router).
+
+Printed: one JSON line with tokens/s for the whole layer, the roofline of the dominant stage
+(the grouped expert GEMMs, timed with HIP events on the stream they run on), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe")
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", action="store_true", help="also time each stage call alone")
+    return ap.parse_args()
+
+
+def event_time_ms(fn, n, torch):
+    """Average GPU time of fn() over n calls, each bracketed by events on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / n
+
+
+def cpu_baseline(cfg, w, x, n_tokens):
+    import numpy as np
+    import workloads
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    n = min(n_tokens, x.shape[0])
+    xs = workloads.to_numpy_f32(x[:n])
+    wo = {k: workloads.to_numpy_f32(v) for k, v in w.items()}
+    cfgO = O.MoEConfig.from_dict(cfg)
+    t0 = time.perf_counter()
+    O.forward(cfgO, wo, xs)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} tokens of the {x.shape[0]}-token batch, full weights, float64 oracle "
+                      f"({dt:.1f} s; {platform.processor() or platform.machine()})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import top_routing_grouped_router_amd as moe
+    import workloads
+
+    torch.cuda.set_device(0)
+    name = args.workload
+    cfg, w, x = workloads.make_workload(name, device="cuda")
+    T = x.shape[0]
+    E, k, h = cfg["num_experts"], cfg["top_k"], cfg["hidden_size"]
+    d, L = cfg["d_model"], cfg["latent_dim"] or 0
+    K = L or d
+    A = T * k
+    layer = moe.MoELayer(cfg, w)
+    y = torch.empty_like(x)
+
+    for _ in range(args.warmup):
+        layer(x, out=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer(x, out=y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    tokens_per_s = T / (ms / 1e3)
+
+    # Dominant stage: the grouped expert GEMMs (tile list, up/gate GEMM + SwiGLU, down GEMM).
+    _, r = layer(x, routing=("expert_offsets", "permutation", "expert_weights"))
+    z = moe.latent_down(cfg, w, x) if L else x
+    offs, perm = r["expert_offsets"], r["permutation"]
+    for _ in range(2):
+        moe.experts_forward(cfg, w, z, offs, perm)
+    gemm_ms = event_time_ms(lambda: moe.experts_forward(cfg, w, z, offs, perm), max(args.steps, 5), torch)
+    gemm_flops = 6.0 * A * K * h
+    achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
+    layer_flops = 2.0 * T * d * E + gemm_flops + (4.0 * T * d * L if L else 0.0)
+
+    out = {
+        "metric": "MoE layer fwd tokens/s + grouped-GEMM % of bf16 MFMA peak, 1xMI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": T, "d_model": d, "num_experts": E, "top_k": k,
+                   "hidden_size": h, "latent_dim": L or None, "gating": cfg["gating_function"],
+                   "router": "fp32", "parallelism": "none (1 GPU)"},
+        "layer_tflops": round(layer_flops / (ms / 1e3) / 1e12, 2),
+        "roofline": {"kernel": "grouped expert GEMMs (up/gate+SwiGLU, down)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "stage_ms": round(gemm_ms, 4), "flops_per_launch": gemm_flops},
+    }
+    if args.stages:
+        st = {}
+        st["router"] = event_time_ms(lambda: moe.router_forward(cfg, w, x, logits=False, scores=False), 5, torch)
+        idx = moe.router_forward(cfg, w, x, logits=False, scores=False)["expert_indices"]
+        st["permute"] = event_time_ms(lambda: moe.permute(cfg, idx), 5, torch)
+        if L:
+            st["latent_down"] = event_time_ms(lambda: moe.latent_down(cfg, w, x), 5, torch)
+        st["experts"] = gemm_ms
+        ya = moe.experts_forward(cfg, w, z, offs, perm)
+        st["combine"] = event_time_ms(lambda: moe.combine(cfg, ya, r["expert_weights"], w.get("norm_weight")), 5,
+                                      torch)
+        if L:
+            n = torch.empty((T, L), dtype=x.dtype, device=x.device)
+            st["latent_up"] = event_time_ms(lambda: moe.latent_up(cfg, w, n), 5, torch)
+        out["stages_ms"] = {k2: round(v, 4) for k2, v in st.items()}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,260 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed Mixture-of-Experts layer forward pass on MI355X (gfx950).
+ *
+ * What the layer computes is defined on the page "Как устроен Olmo-core 3: обучение больших
+ * MoE-моделей" (cited below as [OC3 "<section title>"]):
+ *   router logits in fp32 from an (E, d_model) weight -> gating (softmax / topk_softmax /
+ *   sigmoid + epsilon) -> top-k on score (+ per-expert score_bias), ties to the lower index ->
+ *   weight normalisation and scaling -> optional latent down-projection d_model -> latent_dim
+ *   -> stable permutation of the token copies by expert -> per-expert SwiGLU MLP (grouped
+ *   GEMM, up_factor 2) -> unpermute and weighted combine -> optional bias-free RMSNorm, cast
+ *   and up-projection latent_dim -> d_model.
+ * The 896-expert latent shapes follow "Architecting Trillion-Scale Sparse Multimodal Models:
+ * Design and Training Practices", section 1.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory) of the calling
+ *     process's current device, contiguous, row-major, 16-byte aligned. The caller owns every
+ *     buffer; the library never allocates, frees or synchronises, and keeps no state between
+ *     calls apart from cached device properties.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on it and
+ *     MOE_OK means "enqueued"; results are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before any HIP call. A failed check returns a
+ *     status, enqueues nothing, and moe_last_error_message() (thread-local) says why. A launch
+ *     failure returns MOE_ERR_HIP. Nothing aborts or throws across the ABI.
+ *   - "D" below is the layer storage dtype (cfg.dtype): float for MOE_DTYPE_F32, bfloat16
+ *     (uint16 bit pattern, round-to-nearest-even) for MOE_DTYPE_BF16. The router weight,
+ *     biases, routing weights, logits and scores are always float32.
+ *   - T = number of tokens; E = num_experts; k = top_k; K = latent_dim if set, else d_model;
+ *     h = hidden_size; A = T*k (token-expert assignments). T = 0 is a valid no-op.
+ *   - Results are deterministic: no floating-point atomics anywhere, so repeated calls on the
+ *     same inputs are bitwise identical.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOP_K 16
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,          /* NULL required pointer, bad size, inconsistent config  */
+  MOE_ERR_UNSUPPORTED = 2,          /* valid on the page but not built here (see message)     */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size()                    */
+  MOE_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed             */
+} moe_status_t;
+
+/* [OC3 "Маршрутизация: как роутер выбирает экспертов"]: the three gating functions. */
+typedef enum {
+  MOE_GATING_SOFTMAX = 0,       /* scores = softmax(logits); pick top-k of scores (+bias); weights = scores */
+  MOE_GATING_TOPK_SOFTMAX = 1,  /* pick top-k of logits (+bias); weights = softmax over the k logits        */
+  MOE_GATING_SIGMOID = 2        /* scores = sigmoid(logits) (+eps); pick top-k of scores (+bias)            */
+} moe_gating_t;
+
+/* [OC3 "Как задаётся конфигурация MoE"]: swiglu has up_factor 2. Only SwiGLU is defined on the
+ * pages with its arithmetic ([OC3 "SwiGLU с квантизацией"]); other activations are rejected. */
+typedef enum { MOE_ACT_SWIGLU = 0 } moe_activation_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/*
+ * Layer configuration. Field names follow MoEConfig / MoERouterConfigV2 / LatentMoEConfig
+ * ([OC3 "Как задаётся конфигурация MoE"], [OC3 "Маршрутизация: как роутер выбирает
+ * экспертов"], [OC3 "Латентная проекция экспертов"]). Call moe_config_default() first, then
+ * set fields; struct_size lets the library reject a caller built against another layout.
+ */
+typedef struct moe_config_t {
+  int32_t struct_size;                /* = sizeof(moe_config_t)                               */
+  int32_t num_experts;                /* E, 1..MOE_MAX_EXPERTS (page default 1)               */
+  int64_t d_model;                    /* model width, > 0                                      */
+  int32_t top_k;                      /* k, 1..min(E, MOE_MAX_TOP_K)                           */
+  int32_t gating_function;            /* moe_gating_t                                          */
+  float sigmoid_stability_epsilon;    /* added to sigmoid scores; 0 = unset                    */
+  float normalize_expert_weights;     /* p of the p-norm the k weights are divided by; 0 = off */
+  int32_t restore_weight_scale;       /* nonzero: weights *= top_k                             */
+  float expert_weight_scale;          /* weights *= this; 0 = unset                            */
+  int32_t original_top_k;             /* != top_k: weights *= sqrt(original_top_k/top_k); 0 = unset */
+  int32_t router_bias;                /* nonzero: router linear layer has an (E) bias          */
+  int64_t hidden_size;                /* h, expert hidden width (page default 256)             */
+  int32_t activation;                 /* moe_activation_t                                      */
+  int32_t dtype;                      /* moe_dtype_t: storage dtype D of x, y and expert weights */
+  int64_t latent_dim;                 /* L; 0 = no latent projection                           */
+  int32_t up_proj_input_norm;         /* with latent: nonzero = bias-free RMSNorm before up-proj */
+  float up_proj_input_norm_eps;       /* RMSNorm epsilon (page gives none; default 1e-5)       */
+} moe_config_t;
+
+/*
+ * Layer weights (device pointers, caller-owned, layouts out_features x in_features with the
+ * input dimension contiguous -- the router's (E, d_model) layout of [OC3 "Маршрутизация"]).
+ */
+typedef struct moe_weights_t {
+  const float* router_weight;  /* (E, d_model) fp32, required                                */
+  const float* router_bias;    /* (E) fp32; required iff cfg.router_bias                      */
+  const float* score_bias;     /* (E) fp32 or NULL: added to the selection keys only
+                                  ([OC3 "Счётчики и bias-корректировка"])                      */
+  const void* down_proj;       /* (L, d_model) D; required iff latent_dim                      */
+  const float* up_proj_input_norm_weight; /* (L) fp32 RMSNorm weight g, or NULL = all ones      */
+  const void* up_proj;         /* (d_model, L) D; required iff latent_dim                      */
+  const void* w1;              /* (E, 2h, K) D: rows [0, h) = up, rows [h, 2h) = gate
+                                  ([OC3 "SwiGLU с квантизацией"] splits up then gate)           */
+  const void* w2;              /* (E, K, h) D                                                  */
+} moe_weights_t;
+
+/*
+ * Routing outputs and optional diagnostics. Every pointer may be NULL (not wanted); the
+ * stage calls below say which ones they require.
+ */
+typedef struct moe_routing_t {
+  float* expert_weights;           /* (T, k) fp32 combine weights, j in key-descending order   */
+  int32_t* expert_indices;         /* (T, k) int32 selected experts, key-descending, ties low  */
+  int32_t* batch_size_per_expert;  /* (E) int32 token counts per expert
+                                      ([OC3 "Балансировка нагрузки и вспомогательные штрафы"])  */
+  int32_t* expert_offsets;         /* (E+1) int32 exclusive cumsum of the counts               */
+  int32_t* permutation;            /* (A) int32: sorted position p -> assignment t*k+j         */
+  int32_t* inverse_permutation;    /* (A) int32: assignment t*k+j -> sorted position p          */
+  float* router_logits;            /* (T, E) fp32 logits                                       */
+  float* router_scores;            /* (T, E) fp32 gating scores (softmax or sigmoid+eps)       */
+} moe_routing_t;
+
+/* ------------------------------------------------------------------------ housekeeping */
+
+/* Returns MOE_ABI_VERSION of the built library. */
+MOE_API int moe_abi_version(void);
+
+/* Static description of a status code. Never NULL. */
+MOE_API const char* moe_status_string(moe_status_t status);
+
+/* Message of the last failed call on this thread ("" if none). Valid until the next call. */
+MOE_API const char* moe_last_error_message(void);
+
+/* Fills *cfg with the page defaults ([OC3 "Как задаётся конфигурация MoE"]: num_experts 1,
+ * hidden_size 256) plus: top_k 1, softmax gating, SwiGLU, bf16, no latent, RMSNorm eps 1e-5.
+ * d_model is left 0 and must be set. INVALID_ARG if cfg is NULL. */
+MOE_API moe_status_t moe_config_default(moe_config_t* cfg);
+
+/* Checks a configuration without touching the GPU. INVALID_ARG for values the page rules out
+ * (top_k > num_experts, non-positive sizes, unknown enums); UNSUPPORTED for valid settings
+ * this build does not implement (E > 1024, k > 16, non-SwiGLU, bf16 widths not multiples of
+ * 64: d_model, latent_dim and hidden_size must be multiples of 64 in bf16). */
+MOE_API moe_status_t moe_config_validate(const moe_config_t* cfg);
+
+/* [OC3 "Как задаётся конфигурация MoE"]: total = router (d_model*E, +E with bias) +
+ * 3*latent_dim*h*E, active = total - 3*latent_dim*h*E + 3*latent_dim*h*top_k, where
+ * latent_dim is d_model without a latent projection. Either output pointer may be NULL. */
+MOE_API moe_status_t moe_num_params(const moe_config_t* cfg, int64_t* total, int64_t* active);
+
+/* Bytes of device workspace moe_forward needs for T tokens (also enough for every stage call
+ * with the same cfg and T). T*k must stay below 2^31 (int32 offsets,
+ * [OC3 "Вычисления экспертов и точность"]); INVALID_ARG otherwise. */
+MOE_API moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t num_tokens, size_t* bytes);
+
+/* ------------------------------------------------------------------------ full layer */
+
+/*
+ * The whole forward pass for T tokens:
+ *   x (T, d_model) D  ->  y (T, d_model) D.
+ * routing may be NULL; non-NULL fields receive the routing outputs of this call. ws must
+ * hold at least moe_workspace_size(cfg, T) bytes; its contents on entry do not matter.
+ */
+MOE_API moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* weights, int64_t num_tokens,
+                         const void* x, void* y, moe_routing_t* routing, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ stage calls */
+
+/*
+ * Router: [OC3 "Маршрутизация: как роутер выбирает экспертов"]. x (T, d_model) D is read as
+ * fp32; logits = x * router_weight^T (+ router_bias) in fp32; gating; top-k of the keys
+ * (scores or logits, + score_bias); weights gathered / re-softmaxed, normalised and scaled.
+ * Requires routing->expert_weights and routing->expert_indices; router_logits and
+ * router_scores are filled when non-NULL. Uses the workspace for the logits otherwise.
+ */
+MOE_API moe_status_t moe_router_forward(const moe_config_t* cfg, const moe_weights_t* weights,
+                                int64_t num_tokens, const void* x, moe_routing_t* routing,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Selection and weights from a given gating output -- the injection point that makes the
+ * routing checkable bit for bit. sel_input (T, E) fp32 is the scores for softmax / sigmoid
+ * gating and the logits for topk_softmax ([OC3 "Маршрутизация"]: those are what each gating
+ * selects on); score_bias (E) fp32 or NULL. Key = sel_input + score_bias (one fp32 add);
+ * indices = the k largest keys, largest first, equal keys to the lower index, -0.0 == +0.0,
+ * NaN after every number. Writes expert_indices (T, k) and expert_weights (T, k). No
+ * workspace.
+ */
+MOE_API moe_status_t moe_route_from_scores(const moe_config_t* cfg, int64_t num_tokens,
+                                   const float* sel_input, const float* score_bias,
+                                   int32_t* expert_indices, float* expert_weights, void* stream);
+
+/*
+ * Token counts and the stable permutation: [OC3 "Пересылка токенов между экспертами"] (sort
+ * the expert indices; bins = cumsum of counts) and [OC3 "Балансировка нагрузки и
+ * вспомогательные штрафы"] (per-expert histogram). expert_indices (T, k) int32 in [0, E),
+ * distinct within a row (not checked on the device; out-of-range entries are not counted and
+ * get no position). Outputs (all required): batch_size_per_expert (E), expert_offsets (E+1),
+ * permutation (A), inverse_permutation (A); the permutation is the stable sort of t*k+j by
+ * expert. Uses the workspace.
+ */
+MOE_API moe_status_t moe_permute(const moe_config_t* cfg, int64_t num_tokens,
+                         const int32_t* expert_indices, int32_t* batch_size_per_expert,
+                         int32_t* expert_offsets, int32_t* permutation,
+                         int32_t* inverse_permutation, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Latent down-projection ([OC3 "Латентная проекция экспертов"], prepare_routed_input):
+ * z (T, L) D = x (T, d_model) D * down_proj^T, fp32 accumulation. UNSUPPORTED without latent.
+ */
+MOE_API moe_status_t moe_latent_down(const moe_config_t* cfg, const moe_weights_t* weights,
+                             int64_t num_tokens, const void* x, void* z, void* stream);
+
+/*
+ * Routed experts ([OC3 "Вычисления экспертов и точность"], [OC3 "SwiGLU с квантизацией"]):
+ * for every expert e, the rows p in [offsets[e], offsets[e+1]) of the sorted order take token
+ * t = permutation[p] / k of z (T, K) D, compute H = z_t * w1[e]^T, act = up * gate *
+ * sigmoid(gate) (fp32, stored as D), Y = act * w2[e]^T in fp32 accumulation, rounded to D
+ * (bf16 for bf16 layers: the grouped experts return bf16), and write Y to row
+ * permutation[p] of y_assign (A, K) D -- i.e. y_assign is in assignment order t*k+j. Experts
+ * with no rows read no weights. Uses the workspace.
+ */
+MOE_API moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* weights,
+                                 int64_t num_tokens, const void* z, const int32_t* expert_offsets,
+                                 const int32_t* permutation, void* y_assign, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Unpermute + weighted combine (+ latent restore norm): o[t] = sum_{j<k} expert_weights[t,j] *
+ * y_assign[t*k+j] in fp32, j ascending ([OC3 "Пересылка токенов между экспертами"]: results
+ * return to the original positions). Without latent: out (T, K) D = o. With latent: out
+ * (T, L) D = RMSNorm(o) * g if cfg.up_proj_input_norm, else o, cast to D
+ * ([OC3 "Латентная проекция экспертов"]). weights may be NULL when no norm weight is needed.
+ */
+MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const moe_weights_t* weights,
+                         int64_t num_tokens, const void* y_assign, const float* expert_weights,
+                         void* out, void* stream);
+
+/*
+ * Latent up-projection ([OC3 "Латентная проекция экспертов"], restore_routed_output): y
+ * (T, d_model) D = n (T, L) D * up_proj^T, fp32 accumulation. UNSUPPORTED without latent.
+ */
+MOE_API moe_status_t moe_latent_up(const moe_config_t* cfg, const moe_weights_t* weights,
+                           int64_t num_tokens, const void* n, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,125 @@
+"""Helpers shared by the GPU parity tests: tolerances, comparisons, sampled-oracle evaluation.
+
+Tolerances (stated once, used everywhere):
+  * integer / index outputs: bit-exact;
+  * bf16 layers: max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_F / ||oracle||_F <= 1e-2;
+  * fp32 layers: relative Frobenius <= 1e-5 and max |.| <= 1e-5 * max |oracle|;
+  * fp32 routing weights: |gpu - oracle| <= 4e-6 * max(1, |oracle|) (a few fp32 roundings of
+    the same fp32 inputs).
+The oracle's final y is unrounded (float64); the GPU's y is rounded to the layer dtype.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+
+BF16_MAX_ABS = 2e-2
+BF16_REL_FRO = 1e-2
+F32_REL_FRO = 1e-5
+F32_REL_MAX = 1e-5
+WEIGHT_TOL = 4e-6
+
+
+def np32(t):
+    return workloads.to_numpy_f32(t)
+
+
+def assert_close(got, ref, dtype: str, what: str = ""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if got.size == 0:
+        return
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU values"
+    d = np.abs(got - ref)
+    fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    mx = d.max()
+    if dtype == "bf16":
+        assert mx <= BF16_MAX_ABS and fro <= BF16_REL_FRO, \
+            f"{what}: max-abs {mx:.3e} (<= {BF16_MAX_ABS}), rel-fro {fro:.3e} (<= {BF16_REL_FRO}), max|ref| {np.abs(ref).max():.3f}"
+    else:
+        scale = np.abs(ref).max()
+        assert fro <= F32_REL_FRO and mx <= F32_REL_MAX * max(scale, 1e-30), \
+            f"{what}: rel-fro {fro:.3e} (<= {F32_REL_FRO}), max-abs {mx:.3e} (<= {F32_REL_MAX}*{scale:.3e})"
+
+
+def assert_weights_close(got, ref, what="weights"):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    tol = WEIGHT_TOL * np.maximum(1.0, np.abs(ref))
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} entries off, worst {np.abs(got - ref).max():.3e}"
+
+
+def to_device_weights(w: dict, device="cuda"):
+    return {k: (None if v is None else v.to(device)) for k, v in w.items()}
+
+
+def oracle_inputs(w: dict, experts=None) -> dict:
+    """Host float32 copies of the weights for the oracle; with `experts`, only those experts'
+    matrices (a dict e -> array), copied from wherever the tensors live."""
+    out = {k: np32(v) for k, v in w.items() if k not in ("w1", "w2")}
+    if experts is None:
+        out["w1"], out["w2"] = np32(w["w1"]), np32(w["w2"])
+    else:
+        out["w1"] = {int(e): np32(w["w1"][int(e)]) for e in experts}
+        out["w2"] = {int(e): np32(w["w2"][int(e)]) for e in experts}
+    return out
+
+
+def routing_matches(cfgO: O.MoEConfig, gpu_idx, ref: dict, key_tol: float):
+    """Tokens whose GPU selection differs from the oracle's must be near-ties: every swapped
+    pair of experts has oracle keys within key_tol (the selection is then valid under the
+    GPU's own fp32 rounding). Returns the boolean mask of tokens with identical selections."""
+    gpu_idx = np.asarray(gpu_idx)
+    same = np.all(gpu_idx == ref["idx"], axis=1)
+    keys = ref["keys"]
+    for t in np.nonzero(~same)[0]:
+        g, o = set(gpu_idx[t].tolist()), set(ref["idx"][t].tolist())
+        assert len(g) == cfgO.top_k, f"token {t}: repeated experts {gpu_idx[t]}"
+        if g == o:  # same set, order differs: only possible on an exact/near tie
+            kg = keys[t, gpu_idx[t]]
+            assert np.all(np.abs(np.diff(kg)) <= key_tol) or np.all(np.diff(kg) <= key_tol), t
+            continue
+        for a in g - o:
+            for b in o - g:
+                assert abs(keys[t, a] - keys[t, b]) <= key_tol, \
+                    f"token {t}: gpu picked {a} (key {keys[t, a]}) over {b} (key {keys[t, b]})"
+    return same
+
+
+def check_routing_invariants(cfg: dict, r: dict, T: int):
+    """Properties of the routing outputs that hold at any size (checked on the device)."""
+    E, k = cfg["num_experts"], cfg["top_k"]
+    idx = r["expert_indices"].long()
+    assert idx.shape == (T, k)
+    assert int(idx.min()) >= 0 and int(idx.max()) < E
+    s, _ = torch.sort(idx, dim=1)
+    assert bool((s[:, 1:] != s[:, :-1]).all()), "repeated expert within a token"
+    counts = torch.bincount(idx.flatten(), minlength=E)
+    assert torch.equal(counts.to(torch.int32), r["batch_size_per_expert"])
+    off = torch.zeros(E + 1, dtype=torch.int64, device=idx.device)
+    off[1:] = torch.cumsum(counts, 0)
+    assert torch.equal(off.to(torch.int32), r["expert_offsets"])
+    perm = r["permutation"].long()
+    inv = r["inverse_permutation"].long()
+    A = T * k
+    flat = idx.flatten()
+    assert torch.equal(torch.sort(perm).values, torch.arange(A, device=perm.device))
+    assert torch.equal(inv[perm], torch.arange(A, device=perm.device))
+    # sorted by expert, stable (assignment index increasing within an expert)
+    ep = flat[perm]
+    assert bool((ep[1:] >= ep[:-1]).all())
+    same_e = ep[1:] == ep[:-1]
+    assert bool((perm[1:][same_e] > perm[:-1][same_e]).all())
+
+
+def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
+    g = np.random.default_rng(seed)
+    if T <= n:
+        return np.arange(T)
+    s = set(g.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s))

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point the header
+declares, and validates arguments before any HIP call (so these run without a GPU).
+Parameter counts are checked against the CPU oracle and the golden table."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import workloads
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+moe = pytest.importorskip("top_routing_grouped_router_amd",
+                          reason="HIP library not built (run __graft_entry__.build())")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^MOE_API\s+[\w\s\*]+?\b(moe_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    syms = declared_symbols()
+    for name in ("moe_forward", "moe_router_forward", "moe_route_from_scores", "moe_permute",
+                 "moe_experts_forward", "moe_combine", "moe_latent_down", "moe_latent_up",
+                 "moe_config_default", "moe_config_validate", "moe_num_params",
+                 "moe_workspace_size", "moe_status_string", "moe_last_error_message",
+                 "moe_abi_version"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s(moe_\w+)$", out, flags=re.M))
+    assert set(declared_symbols()) <= exported
+    # nothing but the ABI is exported from the library's own code
+    assert all(s.startswith("moe_") for s in exported)
+
+
+def test_abi_version_and_struct_size():
+    assert moe.abi_version() == 1
+    c = moe._CConfig()
+    assert moe._config_default(ctypes.byref(c)) == 0
+    assert c.struct_size == ctypes.sizeof(moe._CConfig)
+    assert c.num_experts == 1 and c.hidden_size == 256 and c.top_k == 1
+    assert c.dtype == 1 and c.up_proj_input_norm == 1
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_validation_rejects_bad_configs():
+    base = dict(d_model=256, num_experts=8, top_k=2, hidden_size=128)
+    moe.validate(base)
+    bad = [
+        (dict(top_k=9), 1), (dict(d_model=0), 1), (dict(hidden_size=-64), 1),
+        (dict(num_experts=2048, top_k=2), 2), (dict(top_k=17, num_experts=32), 2),
+        (dict(d_model=100), 2), (dict(hidden_size=96), 2), (dict(latent_dim=96), 2),
+        (dict(normalize_expert_weights=-1.0), 1), (dict(sigmoid_stability_epsilon=-1e-6), 1),
+        (dict(dtype="f32", d_model=258), 2),
+    ]
+    for over, status in bad:
+        with pytest.raises(moe.MoEError) as ei:
+            moe.validate({**base, **over})
+        assert ei.value.status == status, over
+    moe.validate({**base, "dtype": "f32", "d_model": 260, "hidden_size": 36})
+    c = moe.MoEConfig.of(base).to_c()
+    c.struct_size = 8
+    assert moe._config_validate(ctypes.byref(c)) == 1
+    assert b"struct_size" in moe._last_error()
+    c = moe.MoEConfig.of(base).to_c()
+    c.activation = 3
+    assert moe._config_validate(ctypes.byref(c)) == 2
+    assert moe._config_validate(None) == 1
+    assert moe._status_string(3) == b"workspace too small"
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_num_params_matches_oracle(name):
+    cfg = workloads.layer_config(name)
+    total, active = moe.num_params(cfg)
+    ref = O.num_params(O.MoEConfig.from_dict(cfg))
+    assert (total, active) == (ref["total"], ref["active"])
+
+
+def test_workspace_size_limits():
+    cfg = workloads.layer_config("olmoe")
+    a = moe.workspace_size(cfg, 1024)
+    b = moe.workspace_size(cfg, 8192)
+    assert 0 < a < b
+    assert moe.workspace_size(cfg, 0) >= 0
+    with pytest.raises(moe.MoEError):
+        moe.workspace_size(cfg, (1 << 31) // 8)
+    with pytest.raises(moe.MoEError):
+        moe.workspace_size(cfg, -1)
+
+
+def test_forward_argument_errors_before_any_gpu_call():
+    cfg = moe.MoEConfig.of(workloads.layer_config("olmoe"))
+    c = cfg.to_c()
+    fake = ctypes.c_void_p(0x10000)
+    w = moe._CWeights()
+    T = 128
+    # missing weights
+    assert moe._forward(ctypes.byref(c), None, T, fake, fake, None, fake, 1 << 40, None) == 1
+    assert b"weights" in moe._last_error()
+    w.router_weight = fake
+    assert moe._forward(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None, fake, 1 << 40, None) == 1
+    assert b"w1" in moe._last_error()
+    w.w1 = fake
+    w.w2 = fake
+    # missing x / workspace
+    assert moe._forward(ctypes.byref(c), ctypes.byref(w), T, None, fake, None, fake, 1 << 40, None) == 1
+    assert moe._forward(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None, None, 1 << 40, None) == 1
+    # short workspace
+    need = moe.workspace_size(cfg, T)
+    assert moe._forward(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None, fake, need - 1, None) == 3
+    # T = 0 is a no-op, T*k too large is rejected
+    assert moe._forward(ctypes.byref(c), ctypes.byref(w), 0, None, None, None, None, 0, None) == 0
+    assert moe._forward(ctypes.byref(c), ctypes.byref(w), 1 << 29, fake, fake, None, fake, 1 << 62, None) == 1
+    # latent layer without its projections
+    lat = moe.MoEConfig.of(workloads.layer_config("latent896")).to_c()
+    assert moe._forward(ctypes.byref(lat), ctypes.byref(w), T, fake, fake, None, fake, 1 << 40, None) == 1
+    assert b"down_proj" in moe._last_error()
+    # stage calls
+    assert moe._route_from_scores(ctypes.byref(c), T, fake, None, None, fake, None) == 1
+    assert moe._latent_down(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None) == 2
+    assert moe._permute(ctypes.byref(c), T, fake, fake, fake, fake, fake, fake, 16, None) == 3

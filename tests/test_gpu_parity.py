@@ -1,0 +1,307 @@
+"""GPU parity of every stage of the MoE layer forward against the CPU oracle, through the C ABI.
+
+Stage checks drive each entry point with inputs drawn by the seeded generators (or produced by
+the oracle from them) and compare element by element:
+  * moe_route_from_scores: indices bit-exact, weights to fp32 rounding (the injection point:
+    both sides select on the same fp32 scores);
+  * moe_permute: counts, offsets, permutation and inverse bit-exact;
+  * moe_router_forward: logits inside the fp32 dot-product error bound, selection equal up to
+    near-ties;
+  * moe_experts_forward / moe_combine / moe_latent_down / moe_latent_up: values to the layer
+    tolerance (see tests/parity.py);
+  * moe_forward: whole-layer parity at reduced shapes (every token) that span several tiles
+    with ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import moe_oracle as O
+from parity import (assert_close, assert_weights_close, check_routing_invariants, np32,
+                    oracle_inputs, routing_matches, to_device_weights)
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("top_routing_grouped_router_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# --------------------------------------------------------------------------- routing
+
+ROUTE_CASES = [
+    # (gating, T, E, k, kind, bias, extra cfg)
+    ("softmax", 1000, 64, 8, "normal", None, dict(normalize_expert_weights=1.0)),
+    ("softmax", 777, 8, 2, "ties", None, {}),
+    ("softmax", 300, 896, 8, "nan", "normal", {}),
+    ("sigmoid", 513, 896, 8, "normal", "normal", dict(sigmoid_stability_epsilon=1e-6)),
+    ("sigmoid", 257, 256, 8, "ties", "zipf", {}),
+    ("topk_softmax", 64, 896, 8, "normal", None, {}),
+    ("topk_softmax", 200, 100, 1, "ties", None, {}),
+    ("softmax", 129, 1024, 16, "nan", None, dict(normalize_expert_weights=2.0, restore_weight_scale=True,
+                                                  expert_weight_scale=1.5, original_top_k=32)),
+    ("sigmoid", 99, 5, 5, "ties", None, {}),
+    ("softmax", 1, 1, 1, "normal", None, {}),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"{c[0]}-T{c[1]}-E{c[2]}-k{c[3]}-{c[4]}")
+def test_route_from_scores_bitexact(case):
+    gating, T, E, k, kind, bias, extra = case
+    banner(f"route_from_scores {case}")
+    cfg = dict(d_model=64, num_experts=E, top_k=k, hidden_size=64, gating_function=gating, dtype="f32",
+               **extra)
+    s = workloads.synthetic_scores(T, E, kind).numpy()
+    cfgO = O.MoEConfig.from_dict(cfg)
+    if gating != "topk_softmax" and kind == "normal":
+        # realistic gating output, made by the oracle from synthetic logits
+        s = O.gating_scores(cfgO, s).astype(np.float32)
+    sb = None
+    if bias == "normal":
+        sb = (np.random.default_rng(E).standard_normal(E) * 0.1).astype(np.float32)
+    elif bias == "zipf":
+        sb = (2.0 * np.log(1.0 / (np.arange(E) + 1.0))).astype(np.float32)
+    ref = O.route_from_scores(cfgO, s, sb)
+    idx, w = moe.route_from_scores(cfg, torch.from_numpy(s).cuda(),
+                                   None if sb is None else torch.from_numpy(sb).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"]), "indices differ"
+    if kind != "nan" or gating == "topk_softmax":
+        # NaN scores give NaN weights on both sides; compare the finite rows
+        pass
+    ref_w, got_w = ref["w"], w.cpu().numpy()
+    fin = np.all(np.isfinite(ref_w), axis=1)
+    assert np.array_equal(np.isfinite(got_w), np.isfinite(ref_w))
+    assert_weights_close(got_w[fin], ref_w[fin])
+
+
+# --------------------------------------------------------------------------- dispatch
+
+PERMUTE_CASES = [(1000, 64, 8, 0.0), (777, 896, 8, 1.0), (33, 5, 5, 0.0), (4097, 256, 8, 2.5),
+                 (1, 16, 4, 0.0), (300, 1024, 16, 0.5), (256, 1, 1, 0.0)]
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES, ids=lambda c: f"T{c[0]}-E{c[1]}-k{c[2]}-skew{c[3]}")
+def test_permute_bitexact(case):
+    T, E, k, skew = case
+    banner(f"permute {case}")
+    idx = workloads.random_distinct_indices(T, E, k, skew=skew)
+    cfg = dict(d_model=64, num_experts=E, top_k=k, hidden_size=64, dtype="bf16")
+    r = moe.permute(cfg, idx.cuda())
+    torch.cuda.synchronize()
+    counts = O.expert_counts(idx.numpy(), E)
+    perm, inv = O.stable_permutation(idx.numpy())
+    assert np.array_equal(r["batch_size_per_expert"].cpu().numpy(), counts)
+    assert np.array_equal(r["expert_offsets"].cpu().numpy(), O.expert_offsets(counts))
+    assert np.array_equal(r["permutation"].cpu().numpy(), perm)
+    assert np.array_equal(r["inverse_permutation"].cpu().numpy(), inv)
+
+
+def test_permute_zero_tokens():
+    cfg = dict(d_model=64, num_experts=7, top_k=2, hidden_size=64)
+    r = moe.permute(cfg, torch.zeros((0, 2), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(r["batch_size_per_expert"].abs().sum()) == 0
+    assert int(r["expert_offsets"].abs().sum()) == 0
+
+
+# --------------------------------------------------------------------------- router
+
+ROUTER_CASES = [
+    ("tiny_f32", None, {}),
+    ("olmoe", 513, dict(d_model=1024, num_experts=64)),
+    ("latent896", 300, dict(d_model=512, latent_dim=256)),
+    ("decode", None, dict(d_model=1024)),
+    ("skewed", 257, dict(d_model=512, num_experts=256)),
+]
+
+
+def _fp32_logit_bound(x, W):
+    """|l_gpu - l_exact| <= gamma_n * sum_i |x_i W_ei| with gamma_n = n u / (1 - n u), u = 2^-24,
+    n = d (sequential accumulation), plus the final fp32 rounding of the oracle (1/2 ulp)."""
+    d = x.shape[1]
+    u = 2.0 ** -24
+    g = d * u / (1 - d * u)
+    return g * (np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
+
+
+@pytest.mark.parametrize("case", ROUTER_CASES, ids=lambda c: c[0])
+def test_router_forward(case):
+    name, T, over = case
+    banner(f"router {case}")
+    cfg, w, x = workloads.make_workload(name, tokens=T, **over)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    wg = to_device_weights(w)
+    r = moe.router_forward(cfg, wg, x.cuda())
+    torch.cuda.synchronize()
+    xr, W = np32(x), np32(w["router_weight"])
+    ref_l = O.router_logits(xr, W, np32(w["router_bias"]))
+    got_l = r["router_logits"].cpu().numpy().astype(np.float64)
+    bound = _fp32_logit_bound(xr, W) + np.abs(ref_l) * 2.0 ** -24
+    assert np.all(np.abs(got_l - ref_l) <= bound), np.max(np.abs(got_l - ref_l) / bound)
+    ref = O.route(cfgO, ref_l, np32(w["score_bias"]))
+    got_s = r["router_scores"].cpu().numpy()
+    assert np.allclose(got_s, ref["scores"], rtol=1e-4, atol=1e-6)
+    key_tol = 1e-4 * max(1.0, float(np.abs(ref["keys"]).max()))
+    same = routing_matches(cfgO, r["expert_indices"].cpu().numpy(), ref, key_tol)
+    assert same.mean() > 0.99
+    assert_weights_close(r["expert_weights"].cpu().numpy()[same], ref["w"][same])
+
+
+# --------------------------------------------------------------------------- experts / combine
+
+EXPERT_CASES = [
+    ("tiny_f32", None, {}),
+    ("olmoe", 777, dict(d_model=512, num_experts=16, top_k=4, hidden_size=256)),  # large tiles
+    ("olmoe", 130, dict(d_model=512, num_experts=64, top_k=8, hidden_size=192)),  # small tiles
+    ("skewed", 600, dict(d_model=256, num_experts=32, top_k=4, hidden_size=320)),  # hot experts
+    ("latent896", 200, dict(d_model=512, latent_dim=128, num_experts=96, top_k=8, hidden_size=128)),
+]
+
+
+def _oracle_routing(cfg, w, x):
+    cfgO = O.MoEConfig.from_dict(cfg)
+    wo = oracle_inputs(w)
+    l = O.router_logits(np32(x), wo["router_weight"], wo["router_bias"])
+    r = O.route(cfgO, l, wo["score_bias"])
+    return cfgO, wo, r
+
+
+@pytest.mark.parametrize("case", EXPERT_CASES, ids=lambda c: f"{c[0]}-{c[1]}")
+def test_experts_forward(case):
+    name, T, over = case
+    banner(f"experts {case}")
+    cfg, w, x = workloads.make_workload(name, tokens=T, **over)
+    cfgO, wo, r = _oracle_routing(cfg, w, x)
+    z = O.prepare_routed_input(cfgO, np32(x), wo["down_proj"])
+    ex = O.run_experts(cfgO, z, r["idx"], wo["w1"], wo["w2"])
+    D = workloads.storage_dtype(cfg)
+    zt = torch.from_numpy(z.astype(np.float32)).to(D).cuda()  # z holds D-representable values
+    y = moe.experts_forward(cfg, to_device_weights(w), zt,
+                            torch.from_numpy(ex["offsets"].astype(np.int32)).cuda(),
+                            torch.from_numpy(ex["perm"].astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    ref_assign = ex["Y"][ex["inv"]]  # assignment order t*k+j
+    assert_close(np32(y), ref_assign, cfg["dtype"], "expert outputs")
+
+
+@pytest.mark.parametrize("case", [("olmoe", 300, dict(d_model=512, num_experts=16, top_k=4, hidden_size=128)),
+                                  ("latent896", 300, dict(d_model=512, latent_dim=256, num_experts=32)),
+                                  ("tiny_f32", None, {}),
+                                  ("latent896", 100, dict(d_model=512, latent_dim=256, num_experts=32,
+                                                          dtype="f32"))],
+                         ids=lambda c: f"{c[0]}-{c[2].get('dtype', '')}")
+def test_combine(case):
+    name, T, over = case
+    banner(f"combine {case}")
+    cfg, w, x = workloads.make_workload(name, tokens=T, **over)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    T = x.shape[0]
+    k, K = cfg["top_k"], (cfg["latent_dim"] or cfg["d_model"])
+    D = workloads.storage_dtype(cfg)
+    g = torch.Generator().manual_seed(7)
+    Y = torch.randn((T * k, K), generator=g).mul_(0.3).to(D)
+    wts = torch.rand((T, k), generator=g, dtype=torch.float32)
+    nw = None
+    if cfg["latent_dim"]:
+        nw = (1.0 + 0.1 * torch.randn((K,), generator=g)).to(torch.float32)
+    out = moe.combine(cfg, Y.cuda(), wts.cuda(), None if nw is None else nw.cuda())
+    torch.cuda.synchronize()
+    Yn = np32(Y)
+    inv = np.arange(T * k)  # y_assign is already in assignment order
+    o = O.combine(cfgO, Yn, inv, wts.numpy())
+    if cfg["latent_dim"]:
+        ref = O.restore_routed_output(cfgO, o, None if nw is None else nw.numpy(),
+                                      np.eye(K, dtype=np.float32))["n"]
+    else:
+        ref = o
+    assert_close(np32(out), ref, cfg["dtype"], "combine")
+
+
+@pytest.mark.parametrize("T", [1, 64, 333])
+def test_latent_projections(T):
+    banner(f"latent projections T={T}")
+    cfg, w, x = workloads.make_workload("latent896", tokens=T, d_model=1024, latent_dim=256,
+                                        num_experts=8)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    wg = to_device_weights(w)
+    z = moe.latent_down(cfg, wg, x.cuda())
+    n = torch.randn((T, 256), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    y = moe.latent_up(cfg, wg, n.cuda())
+    torch.cuda.synchronize()
+    assert_close(np32(z), O.prepare_routed_input(cfgO, np32(x), np32(w["down_proj"])), "bf16", "down")
+    assert_close(np32(y), np32(n).astype(np.float64) @ np32(w["up_proj"]).astype(np.float64).T, "bf16", "up")
+
+
+# --------------------------------------------------------------------------- whole layer
+
+LAYER_CASES = [
+    ("tiny_f32", None, {}),
+    ("tiny_f32", 37, dict(num_experts=8, top_k=8)),                       # k = E
+    ("tiny_f32", 50, dict(num_experts=1, top_k=1)),                       # one expert
+    ("olmoe", 600, dict(d_model=512, num_experts=16, top_k=4, hidden_size=256)),
+    ("olmoe", 96, dict(d_model=1024, hidden_size=512)),                   # 64 experts, few rows each
+    ("latent896", 400, dict(d_model=1024, latent_dim=256, num_experts=128, hidden_size=128)),
+    ("skewed", 700, dict(d_model=512, num_experts=64, top_k=8, hidden_size=256)),
+    ("decode", 3, dict(d_model=512, latent_dim=128, num_experts=64, hidden_size=64)),
+    ("decode", None, dict(d_model=1024, latent_dim=256, num_experts=896, hidden_size=128)),
+    ("latent896", 257, dict(d_model=512, latent_dim=128, num_experts=64, hidden_size=64,
+                            up_proj_input_norm=False)),
+    ("olmoe", 200, dict(d_model=256, num_experts=12, top_k=3, hidden_size=128, gating_function="topk_softmax",
+                        restore_weight_scale=True, router_bias=True)),
+]
+
+
+def run_layer_case(name, T, over):
+    cfg, w, x = workloads.make_workload(name, tokens=T, **over)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    layer = moe.MoELayer(cfg, to_device_weights(w))
+    y, r = layer(x.cuda(), routing=True)
+    torch.cuda.synchronize()
+    T = x.shape[0]
+    check_routing_invariants(cfg, r, T)
+    ref = O.forward(cfgO, oracle_inputs(w), np32(x))
+    key_tol = 1e-4 * max(1.0, float(np.abs(ref["keys"]).max()))
+    same = routing_matches(cfgO, r["expert_indices"].cpu().numpy(), ref, key_tol)
+    assert same.mean() >= 0.99
+    assert_close(np32(y)[same], ref["y"][same], cfg["dtype"], f"layer {name}")
+    return cfg, y
+
+
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{'-'.join(f'{k}{v}' for k, v in c[2].items())}")
+def test_layer_parity(case):
+    banner(f"layer {case}")
+    run_layer_case(*case)
+
+
+def test_layer_deterministic():
+    banner("determinism")
+    cfg, w, x = workloads.make_workload("olmoe", tokens=500, d_model=512, num_experts=16, top_k=4,
+                                        hidden_size=256)
+    layer = moe.MoELayer(cfg, to_device_weights(w))
+    xc = x.cuda()
+    y1, r1 = layer(xc, routing=True)
+    y2, r2 = layer(xc, routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_zero_tokens():
+    cfg, w, x = workloads.make_workload("olmoe", tokens=0, d_model=256, num_experts=4, top_k=2,
+                                        hidden_size=64)
+    layer = moe.MoELayer(cfg, to_device_weights(w))
+    y = layer(x.cuda())
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)

@@ -1,0 +1,556 @@
+// C ABI of the MoE layer library: validation, parameter counts, workspace layout and the
+// launch sequence of the forward pass. Every argument check runs on the host before any HIP
+// call, so the error paths are testable without a GPU.
+//
+// Layer definition: "Как устроен Olmo-core 3: обучение больших MoE-моделей" (sections
+// "Как задаётся конфигурация MoE", "Латентная проекция экспертов", "Маршрутизация: как
+// роутер выбирает экспертов", "Пересылка токенов между экспертами", "Вычисления экспертов и
+// точность", "SwiGLU с квантизацией").
+#include <math.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+moe_status_t ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define MOE_TRY_HIP(expr, where)              \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+bool finite(float v) { return isfinite(v); }
+
+moe_status_t validate_config(const moe_config_t* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->struct_size != static_cast<int32_t>(sizeof(moe_config_t)))
+    return fail(MOE_ERR_INVALID_ARG, "config struct_size does not match this library's moe_config_t");
+  if (c->d_model <= 0) return fail(MOE_ERR_INVALID_ARG, "d_model must be positive");
+  if (c->num_experts <= 0) return fail(MOE_ERR_INVALID_ARG, "num_experts must be positive");
+  if (c->top_k <= 0) return fail(MOE_ERR_INVALID_ARG, "top_k must be positive");
+  if (c->top_k > c->num_experts) return fail(MOE_ERR_INVALID_ARG, "top_k exceeds num_experts");
+  if (c->hidden_size <= 0) return fail(MOE_ERR_INVALID_ARG, "hidden_size must be positive");
+  if (c->latent_dim < 0) return fail(MOE_ERR_INVALID_ARG, "latent_dim must be >= 0");
+  if (c->gating_function < MOE_GATING_SOFTMAX || c->gating_function > MOE_GATING_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gating_function");
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (!finite(c->sigmoid_stability_epsilon) || c->sigmoid_stability_epsilon < 0.f)
+    return fail(MOE_ERR_INVALID_ARG, "sigmoid_stability_epsilon must be finite and >= 0");
+  if (!finite(c->normalize_expert_weights) || c->normalize_expert_weights < 0.f)
+    return fail(MOE_ERR_INVALID_ARG, "normalize_expert_weights (p) must be finite and >= 0");
+  if (!finite(c->expert_weight_scale)) return fail(MOE_ERR_INVALID_ARG, "expert_weight_scale must be finite");
+  if (c->original_top_k < 0) return fail(MOE_ERR_INVALID_ARG, "original_top_k must be >= 0");
+  if (!finite(c->up_proj_input_norm_eps) || c->up_proj_input_norm_eps < 0.f)
+    return fail(MOE_ERR_INVALID_ARG, "up_proj_input_norm_eps must be finite and >= 0");
+  if (c->activation != MOE_ACT_SWIGLU)
+    return fail(MOE_ERR_UNSUPPORTED, "only the swiglu activation is implemented");
+  if (c->num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts above 1024 is not supported");
+  if (c->top_k > MOE_MAX_TOP_K) return fail(MOE_ERR_UNSUPPORTED, "top_k above 16 is not supported");
+  const int64_t mult = c->dtype == MOE_DTYPE_BF16 ? 64 : 4;
+  const char* mult_msg = c->dtype == MOE_DTYPE_BF16 ? "64 for bf16" : "4 for f32";
+  if (c->d_model % mult || c->hidden_size % mult || c->latent_dim % mult)
+    return fail(MOE_ERR_UNSUPPORTED,
+                std::string("d_model, hidden_size and latent_dim must be multiples of ") + mult_msg);
+  const int64_t K = c->latent_dim ? c->latent_dim : c->d_model;
+  const int64_t kmax = c->dtype == MOE_DTYPE_BF16 ? 16384 : 8192;
+  if (K > kmax)
+    return fail(MOE_ERR_UNSUPPORTED, "expert width (latent_dim or d_model) above 16384 (bf16) / 8192 (f32)");
+  if (c->d_model > (int64_t(1) << 30) || c->hidden_size > (int64_t(1) << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "dimension too large");
+  return ok();
+}
+
+Layer make_layer(const moe_config_t* c, int64_t T) {
+  Layer ly{};
+  ly.T = T;
+  ly.d = c->d_model;
+  ly.E = c->num_experts;
+  ly.k = c->top_k;
+  ly.h = c->hidden_size;
+  ly.L = c->latent_dim;
+  ly.K = c->latent_dim ? c->latent_dim : c->d_model;
+  ly.gating = c->gating_function;
+  ly.bf16 = c->dtype == MOE_DTYPE_BF16;
+  ly.sig_eps = c->sigmoid_stability_epsilon;
+  ly.norm_p = c->normalize_expert_weights;
+  ly.restore_scale = c->restore_weight_scale != 0;
+  ly.ews = c->expert_weight_scale;
+  ly.orig_k = c->original_top_k;
+  ly.router_bias = c->router_bias != 0;
+  ly.up_norm = c->up_proj_input_norm != 0;
+  ly.norm_eps = c->up_proj_input_norm_eps;
+  return ly;
+}
+
+moe_status_t check_tokens(const moe_config_t* c, int64_t T) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens * top_k must be below 2^31 (int32 offsets)");
+  if (T * static_cast<int64_t>(c->num_experts) >= (int64_t(1) << 40))
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens * num_experts too large");
+  if (c->dtype == MOE_DTYPE_BF16) {
+    // The bf16 MFMA GEMM addresses each operand (and each expert's weights) with 32-bit byte
+    // offsets: every one must stay below 4 GiB.
+    const int64_t K = c->latent_dim ? c->latent_dim : c->d_model;
+    const int64_t A = T * c->top_k;
+    const int64_t lim = int64_t(1) << 31;  // elements of 2 bytes
+    if (T * c->d_model >= lim || T * K >= lim || A * c->hidden_size >= lim || A * K >= lim ||
+        2 * c->hidden_size * K >= lim || c->d_model * K >= lim)
+      return fail(MOE_ERR_UNSUPPORTED, "a bf16 GEMM operand would exceed 4 GiB; split the batch");
+  }
+  return MOE_OK;
+}
+
+size_t elem_size(const Layer& ly) { return ly.bf16 ? 2 : 4; }
+
+// M-tile height the expert GEMMs use for this layer and token count.
+int expert_variant(const Layer& ly) {
+  const double mean = static_cast<double>(ly.T) * ly.k / ly.E;
+  return gemm_bf16_pick_variant(mean);
+}
+int expert_tile_m(const Layer& ly) { return ly.bf16 ? gemm_bf16_tile_m(expert_variant(ly)) : kF32TileM; }
+int dense_variant(int64_t rows) { return gemm_bf16_pick_variant(static_cast<double>(rows)); }
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  }
+};
+
+struct WsLayout {
+  size_t logits, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, z, act, yassign, total;
+  int32_t tile_cap;
+};
+
+WsLayout ws_layout(const Layer& ly) {
+  WsLayout w{};
+  Carve c;
+  const size_t T = static_cast<size_t>(ly.T), E = static_cast<size_t>(ly.E), A = T * ly.k;
+  const size_t es = elem_size(ly);
+  const int bm = expert_tile_m(ly);
+  w.tile_cap = static_cast<int32_t>((A + bm - 1) / bm + E);
+  w.logits = c.take(T * E * 4);
+  w.idx = c.take(A * 4);
+  w.w = c.take(A * 4);
+  w.counts = c.take(E * 4);
+  w.offsets = c.take((E + 1) * 4);
+  w.perm = c.take(A * 4);
+  w.inv = c.take(A * 4);
+  w.scratch = c.take(dispatch_scratch_bytes(ly));
+  w.tcount = c.take(4);
+  w.texpert = c.take(static_cast<size_t>(w.tile_cap) * 4);
+  w.trow0 = c.take(static_cast<size_t>(w.tile_cap) * 4);
+  w.trows = c.take(static_cast<size_t>(w.tile_cap) * 4);
+  w.z = c.take(ly.L ? T * static_cast<size_t>(ly.L) * es : 0);
+  w.act = c.take(A * static_cast<size_t>(ly.h) * es);
+  w.yassign = c.take(A * static_cast<size_t>(ly.K) * es);
+  w.total = c.off;
+  return w;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<unsigned char*>(ws) + off);
+}
+
+TileList tiles_of(void* ws, const WsLayout& w) {
+  TileList t;
+  t.count = at<int32_t>(ws, w.tcount);
+  t.expert = at<int32_t>(ws, w.texpert);
+  t.row0 = at<int32_t>(ws, w.trow0);
+  t.rows = at<int32_t>(ws, w.trows);
+  t.cap = w.tile_cap;
+  return t;
+}
+
+moe_status_t need(const void* p, const char* what) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, std::string(what) + " is NULL");
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool router, bool latent,
+                           bool experts) {
+  moe_status_t st;
+  if ((st = need(w, "weights")) != MOE_OK) return st;
+  if (router) {
+    if ((st = need(w->router_weight, "weights->router_weight")) != MOE_OK) return st;
+    if (c->router_bias && (st = need(w->router_bias, "weights->router_bias")) != MOE_OK) return st;
+  }
+  if (latent && c->latent_dim) {
+    if ((st = need(w->down_proj, "weights->down_proj")) != MOE_OK) return st;
+    if ((st = need(w->up_proj, "weights->up_proj")) != MOE_OK) return st;
+  }
+  if (experts) {
+    if ((st = need(w->w1, "weights->w1")) != MOE_OK) return st;
+    if ((st = need(w->w2, "weights->w2")) != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+hipError_t run_dense(const Layer& ly, int64_t rows, const void* A, int64_t lda, const void* B, int64_t N,
+                     int64_t Kd, void* C, hipStream_t s) {
+  GemmCall c{};
+  c.A = A;
+  c.lda = lda;
+  c.B = B;
+  c.ldb = Kd;
+  c.C = C;
+  c.ldc = N;
+  c.N = N;
+  c.Kd = Kd;
+  c.dense_M = rows;
+  c.a_rows = rows;
+  c.c_rows = rows;
+  c.rows_bound = rows;
+  if (ly.bf16) return launch_gemm_bf16(c, dense_variant(rows), s);
+  return launch_gemm_f32(c, false, nullptr, s);
+}
+
+hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, const TileList& tiles,
+                       const void* w1, const void* w2, void* act, void* yassign, hipStream_t s) {
+  const int64_t A = ly.T * ly.k;
+  GemmCall g1{};
+  g1.A = z;
+  g1.lda = ly.K;
+  g1.gather = perm;
+  g1.gather_div = ly.k;
+  g1.B = w1;
+  g1.ldb = ly.K;
+  g1.b_group_stride = 2 * ly.h * ly.K;
+  g1.C = act;
+  g1.ldc = ly.h;
+  g1.N = ly.h;
+  g1.Kd = ly.K;
+  g1.swiglu_h = ly.h;
+  g1.tiles = tiles;
+  g1.a_rows = ly.T;
+  g1.c_rows = A;
+  g1.rows_bound = A;
+  GemmCall g2{};
+  g2.A = act;
+  g2.lda = ly.h;
+  g2.B = w2;
+  g2.ldb = ly.h;
+  g2.b_group_stride = ly.K * ly.h;
+  g2.C = yassign;
+  g2.ldc = ly.K;
+  g2.scatter = perm;
+  g2.N = ly.K;
+  g2.Kd = ly.h;
+  g2.tiles = tiles;
+  g2.a_rows = A;
+  g2.c_rows = A;
+  g2.rows_bound = A;
+  hipError_t e;
+  if (ly.bf16) {
+    const int v = expert_variant(ly);
+    if ((e = launch_gemm_bf16(g1, v, s)) != hipSuccess) return e;
+    return launch_gemm_bf16(g2, v, s);
+  }
+  if ((e = launch_gemm_f32(g1, false, nullptr, s)) != hipSuccess) return e;
+  return launch_gemm_f32(g2, false, nullptr, s);
+}
+
+std::mutex g_dev_mu;
+std::vector<int> g_cu_counts;
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (static_cast<int>(g_cu_counts.size()) <= dev) g_cu_counts.resize(dev + 1, 0);
+  if (g_cu_counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_counts[dev] = n;
+  }
+  return g_cu_counts[dev];
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error_message(void) { return g_last_error.c_str(); }
+
+moe_status_t moe_config_default(moe_config_t* cfg) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  *cfg = moe_config_t{};
+  cfg->struct_size = sizeof(moe_config_t);
+  cfg->num_experts = 1;
+  cfg->top_k = 1;
+  cfg->hidden_size = 256;
+  cfg->gating_function = MOE_GATING_SOFTMAX;
+  cfg->activation = MOE_ACT_SWIGLU;
+  cfg->dtype = MOE_DTYPE_BF16;
+  cfg->up_proj_input_norm = 1;
+  cfg->up_proj_input_norm_eps = 1e-5f;
+  return ok();
+}
+
+moe_status_t moe_config_validate(const moe_config_t* cfg) { return validate_config(cfg); }
+
+moe_status_t moe_num_params(const moe_config_t* c, int64_t* total, int64_t* active) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  const int64_t L = c->latent_dim ? c->latent_dim : c->d_model;
+  const int64_t router = c->d_model * c->num_experts + (c->router_bias ? c->num_experts : 0);
+  const int64_t up_factor = 2;  // swiglu
+  const int64_t per_expert = (up_factor + 1) * L * c->hidden_size;
+  const int64_t tot = router + per_expert * c->num_experts;
+  if (total) *total = tot;
+  if (active) *active = tot - 3 * L * c->hidden_size * c->num_experts + 3 * L * c->hidden_size * c->top_k;
+  return ok();
+}
+
+moe_status_t moe_workspace_size(const moe_config_t* c, int64_t T, size_t* bytes) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(make_layer(c, T)).total;
+  return ok();
+}
+
+moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* y,
+                         moe_routing_t* routing, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = check_weights(c, w, true, true, true)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(x, "x")) != MOE_OK) return st;
+  if ((st = need(y, "y")) != MOE_OK) return st;
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  const WsLayout L = ws_layout(ly);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
+                                                 std::to_string(L.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe_routing_t r{};
+  if (routing) r = *routing;
+  float* logits = r.router_logits ? r.router_logits : at<float>(ws, L.logits);
+  int32_t* idx = r.expert_indices ? r.expert_indices : at<int32_t>(ws, L.idx);
+  float* wts = r.expert_weights ? r.expert_weights : at<float>(ws, L.w);
+  int32_t* counts = r.batch_size_per_expert ? r.batch_size_per_expert : at<int32_t>(ws, L.counts);
+  int32_t* offsets = r.expert_offsets ? r.expert_offsets : at<int32_t>(ws, L.offsets);
+  int32_t* perm = r.permutation ? r.permutation : at<int32_t>(ws, L.perm);
+  int32_t* inv = r.inverse_permutation ? r.inverse_permutation : at<int32_t>(ws, L.inv);
+  const TileList tiles = tiles_of(ws, L);
+
+  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, w->router_bias, logits, s), "router logits");
+  MOE_TRY_HIP(launch_gate_topk(ly, logits, false, w->score_bias, idx, wts, r.router_scores, s), "gating/top-k");
+  MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles,
+                              expert_tile_m(ly), s),
+              "dispatch");
+  const void* z = x;
+  if (ly.L) {
+    MOE_TRY_HIP(run_dense(ly, T, x, ly.d, w->down_proj, ly.L, ly.d, at<void>(ws, L.z), s), "latent down");
+    z = at<void>(ws, L.z);
+  }
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), at<void>(ws, L.yassign), s),
+              "experts");
+  if (ly.L) {
+    void* n = at<void>(ws, L.z);  // z is dead after the first expert GEMM
+    MOE_TRY_HIP(launch_combine(ly, at<void>(ws, L.yassign), wts, w->up_proj_input_norm_weight, ly.up_norm, n, s),
+                "combine");
+    MOE_TRY_HIP(run_dense(ly, T, n, ly.L, w->up_proj, ly.d, ly.L, y, s), "latent up");
+  } else {
+    MOE_TRY_HIP(launch_combine(ly, at<void>(ws, L.yassign), wts, nullptr, false, y, s), "combine");
+  }
+  return ok();
+}
+
+moe_status_t moe_router_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x,
+                                moe_routing_t* routing, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = check_weights(c, w, true, false, false)) != MOE_OK) return st;
+  if ((st = need(routing, "routing")) != MOE_OK) return st;
+  if ((st = need(routing->expert_indices, "routing->expert_indices")) != MOE_OK) return st;
+  if ((st = need(routing->expert_weights, "routing->expert_weights")) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(x, "x")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  float* logits = routing->router_logits;
+  if (!logits) {
+    if ((st = need(ws, "workspace (needed when routing->router_logits is NULL)")) != MOE_OK) return st;
+    const WsLayout L = ws_layout(ly);
+    if (ws_bytes < L.logits + static_cast<size_t>(T) * ly.E * 4)
+      return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the router logits");
+    logits = at<float>(ws, L.logits);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, w->router_bias, logits, s), "router logits");
+  MOE_TRY_HIP(launch_gate_topk(ly, logits, false, w->score_bias, routing->expert_indices, routing->expert_weights,
+                               routing->router_scores, s),
+              "gating/top-k");
+  return ok();
+}
+
+moe_status_t moe_route_from_scores(const moe_config_t* c, int64_t T, const float* sel_input,
+                                   const float* score_bias, int32_t* expert_indices, float* expert_weights,
+                                   void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = need(expert_indices, "expert_indices")) != MOE_OK) return st;
+  if ((st = need(expert_weights, "expert_weights")) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(sel_input, "sel_input")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  MOE_TRY_HIP(launch_gate_topk(ly, sel_input, true, score_bias, expert_indices, expert_weights, nullptr,
+                               static_cast<hipStream_t>(stream)),
+              "route from scores");
+  return ok();
+}
+
+moe_status_t moe_permute(const moe_config_t* c, int64_t T, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = need(counts, "batch_size_per_expert")) != MOE_OK) return st;
+  if ((st = need(offsets, "expert_offsets")) != MOE_OK) return st;
+  if ((st = need(perm, "permutation")) != MOE_OK) return st;
+  if ((st = need(inv, "inverse_permutation")) != MOE_OK) return st;
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  const WsLayout L = ws_layout(ly);
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    MOE_TRY_HIP(hipMemsetAsync(counts, 0, sizeof(int32_t) * ly.E, s), "zero counts");
+    MOE_TRY_HIP(hipMemsetAsync(offsets, 0, sizeof(int32_t) * (ly.E + 1), s), "zero offsets");
+    return ok();
+  }
+  if ((st = need(idx, "expert_indices")) != MOE_OK) return st;
+  MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles_of(ws, L),
+                              expert_tile_m(ly), s),
+              "dispatch");
+  return ok();
+}
+
+moe_status_t moe_latent_down(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* z,
+                             void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if (!c->latent_dim) return fail(MOE_ERR_UNSUPPORTED, "latent_down needs latent_dim > 0");
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = need(w, "weights")) != MOE_OK) return st;
+  if ((st = need(w->down_proj, "weights->down_proj")) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(x, "x")) != MOE_OK) return st;
+  if ((st = need(z, "z")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  MOE_TRY_HIP(run_dense(ly, T, x, ly.d, w->down_proj, ly.L, ly.d, z, static_cast<hipStream_t>(stream)),
+              "latent down");
+  return ok();
+}
+
+moe_status_t moe_experts_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* z,
+                                 const int32_t* offsets, const int32_t* perm, void* y_assign, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = check_weights(c, w, false, false, true)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(z, "z")) != MOE_OK) return st;
+  if ((st = need(offsets, "expert_offsets")) != MOE_OK) return st;
+  if ((st = need(perm, "permutation")) != MOE_OK) return st;
+  if ((st = need(y_assign, "y_assign")) != MOE_OK) return st;
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  const WsLayout L = ws_layout(ly);
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const TileList tiles = tiles_of(ws, L);
+  MOE_TRY_HIP(launch_build_tiles(ly, offsets, tiles, expert_tile_m(ly), s), "tile list");
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), y_assign, s), "experts");
+  return ok();
+}
+
+moe_status_t moe_combine(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* y_assign,
+                         const float* expert_weights, void* out, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(y_assign, "y_assign")) != MOE_OK) return st;
+  if ((st = need(expert_weights, "expert_weights")) != MOE_OK) return st;
+  if ((st = need(out, "out")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  const bool norm = ly.L && ly.up_norm;
+  const float* g = (norm && w) ? w->up_proj_input_norm_weight : nullptr;
+  MOE_TRY_HIP(launch_combine(ly, y_assign, expert_weights, g, norm, out, static_cast<hipStream_t>(stream)),
+              "combine");
+  return ok();
+}
+
+moe_status_t moe_latent_up(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* n, void* y,
+                           void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if (!c->latent_dim) return fail(MOE_ERR_UNSUPPORTED, "latent_up needs latent_dim > 0");
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = need(w, "weights")) != MOE_OK) return st;
+  if ((st = need(w->up_proj, "weights->up_proj")) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(n, "n")) != MOE_OK) return st;
+  if ((st = need(y, "y")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  MOE_TRY_HIP(run_dense(ly, T, n, ly.L, w->up_proj, ly.d, ly.L, y, static_cast<hipStream_t>(stream)),
+              "latent up");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// Unpermute + weighted combine (+ the latent restore norm).
+//
+// "Как устроен Olmo-core 3: обучение больших MoE-моделей":
+//   * section "Пересылка токенов между экспертами": expert results return to their original
+//     positions (a scatter with the saved indices). The grouped GEMM already wrote each
+//     result to its assignment row t*k + j, so a token's k results are contiguous here;
+//   * the router's weights scale each result and the k results are summed, in j order, in
+//     fp32: o[t] = sum_j w[t,j] * Y[t*k+j];
+//   * section "Латентная проекция экспертов": with a latent projection, the up-projection
+//     input is normalised (bias-free RMSNorm by default: n = o / sqrt(mean(o^2) + eps) * g)
+//     and cast to the up-projection weight's dtype.
+// One block per token, 16-byte loads and stores, fp32 math. HBM-bound: it reads k*K and
+// writes K elements per token.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxChunks = 8;  // per thread: K <= 256 * 8 * (16 / sizeof(T))
+
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float* v) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(uint16_t* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = f32_to_bf16_bits(v[2 * i]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* v) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  __device__ static void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <typename T, bool NORM>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__ y, const float* __restrict__ w,
+                                                           const float* __restrict__ g, T* __restrict__ out,
+                                                           int k, int K, float eps) {
+  constexpr int V = Vec16<T>::N;
+  const int64_t t = blockIdx.x;
+  const int nch = K / V;
+  float o[kMaxChunks][V];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+#pragma unroll
+    for (int q = 0; q < V; ++q) o[c][q] = 0.f;
+
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const T* yr = y + (t * k + j) * static_cast<int64_t>(K);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int ci = threadIdx.x + c * kThreads;
+      if (ci < nch) {
+        float v[V];
+        Vec16<T>::load(yr + ci * V, v);
+#pragma unroll
+        for (int q = 0; q < V; ++q) o[c][q] = fmaf(wj, v[q], o[c][q]);
+      }
+    }
+  }
+
+  float scale = 1.f;
+  if (NORM) {
+    __shared__ float red[kThreads / kWave];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int ci = threadIdx.x + c * kThreads;
+      if (ci < nch) {
+#pragma unroll
+        for (int q = 0; q < V; ++q) ss = fmaf(o[c][q], o[c][q], ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kThreads / kWave; ++i) tot += red[i];
+    scale = 1.f / sqrtf(tot / static_cast<float>(K) + eps);
+  }
+
+  T* orow = out + t * static_cast<int64_t>(K);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int ci = threadIdx.x + c * kThreads;
+    if (ci < nch) {
+      float v[V];
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        float x = o[c][q];
+        if (NORM) {
+          x = x * scale;
+          if (g) x = x * g[ci * V + q];
+        }
+        v[q] = x;
+      }
+      Vec16<T>::store(orow + ci * V, v);
+    }
+  }
+}
+
+template <typename T>
+void launch_t(const Layer& ly, const void* y, const float* w, const float* g, bool norm, void* out,
+              hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ly.T)), block(kThreads);
+  const int K = static_cast<int>(ly.K);
+  if (norm)
+    hipLaunchKernelGGL((combine_kernel<T, true>), grid, block, 0, s, static_cast<const T*>(y), w, g,
+                       static_cast<T*>(out), ly.k, K, ly.norm_eps);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, false>), grid, block, 0, s, static_cast<const T*>(y), w, g,
+                       static_cast<T*>(out), ly.k, K, ly.norm_eps);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Layer& ly, const void* y_assign, const float* w,
+                          const float* norm_weight, bool apply_norm, void* out, hipStream_t s) {
+  if (ly.T <= 0) return hipSuccess;
+  if (ly.bf16) launch_t<uint16_t>(ly, y_assign, w, norm_weight, apply_norm, out, s);
+  else launch_t<float>(ly, y_assign, w, norm_weight, apply_norm, out, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

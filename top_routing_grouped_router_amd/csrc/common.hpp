@@ -1,0 +1,158 @@
+// Internal declarations shared by the HIP translation units of the MoE layer library.
+// gfx950 (CDNA4) only: 64-wide wavefronts, MFMA matrix cores, 160 KB LDS per CU, 8 XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_mi355x.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 (bit patterns)
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Element access for the two storage dtypes.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  using storage = float;
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+  using storage = uint16_t;
+  __device__ static float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  __device__ static void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+    uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- layer description
+
+// Resolved, validated layer description used by the launchers (host side).
+struct Layer {
+  int64_t T;      // tokens
+  int64_t d;      // d_model
+  int32_t E;      // experts
+  int32_t k;      // top_k
+  int64_t h;      // hidden
+  int64_t L;      // latent (0 = none)
+  int64_t K;      // expert input width (L or d)
+  int gating;     // moe_gating_t
+  bool bf16;      // storage dtype
+  float sig_eps;
+  float norm_p;
+  bool restore_scale;
+  float ews;
+  int32_t orig_k;
+  bool router_bias;
+  bool up_norm;
+  float norm_eps;
+};
+
+// Per-expert M-tile list consumed by the grouped GEMMs (device memory, built on the device).
+struct TileList {
+  int32_t* count;   // [1]   number of M-tiles
+  int32_t* expert;  // [cap] expert of each M-tile
+  int32_t* row0;    // [cap] first sorted row of each M-tile
+  int32_t* rows;    // [cap] valid rows (<= BM)
+  int32_t cap;
+};
+
+// Grid-wide properties cached per device.
+int device_cu_count();
+
+// ---------------------------------------------------------------- launchers (host)
+// Every launcher enqueues on `s` and returns hipSuccess or the launch error.
+
+// Router logits: logits (T,E) f32 = x (T,d) * Wr^T (+ bias). x is f32 or bf16 bits.
+hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, const float* br,
+                                float* logits, hipStream_t s);
+
+// Gating + top-k + weights from logits (from_scores = false) or from the gating output
+// (from_scores = true: scores for softmax/sigmoid, logits for topk_softmax).
+hipError_t launch_gate_topk(const Layer& ly, const float* input, bool from_scores,
+                            const float* score_bias, int32_t* idx, float* w, float* scores_out,
+                            hipStream_t s);
+
+// Histogram, stable permutation and the M-tile list (tile height bm).
+size_t dispatch_scratch_bytes(const Layer& ly);
+hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
+                           int bm, hipStream_t s);
+// Only the M-tile list, from existing offsets.
+hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
+                              int bm, hipStream_t s);
+
+// GEMM variants. All operands are "NT": A (rows, Kd) and B (N, Kd), Kd contiguous.
+struct GemmCall {
+  const void* A;            // token rows (f32 or bf16 bits)
+  int64_t lda;
+  const int32_t* gather;    // logical sorted row p -> A row gather[p] / gather_div (or NULL)
+  int32_t gather_div;
+  const void* B;            // weight rows
+  int64_t ldb;
+  int64_t b_group_stride;   // elements between consecutive experts' weights
+  void* C;                  // output
+  int64_t ldc;
+  const int32_t* scatter;   // logical sorted row p -> output row scatter[p] (or NULL)
+  int64_t N;                // output columns (SwiGLU: act columns = h)
+  int64_t Kd;               // contraction length
+  int64_t swiglu_h;         // > 0: SwiGLU epilogue, gate rows start at +swiglu_h
+  int64_t dense_M;          // > 0: dense GEMM with this many rows (tiles ignored)
+  TileList tiles;           // grouped mode
+  // Bounds used to clamp every row index a kernel derives from device data, so that a
+  // corrupt index can never address memory outside the operands.
+  int64_t a_rows;           // rows of A
+  int64_t c_rows;           // rows of C
+  int64_t rows_bound;       // logical (sorted) rows: dense_M or T*k
+};
+
+// bf16 MFMA GEMM; returns the M-tile height it was instantiated with for the chosen variant.
+int gemm_bf16_tile_m(int variant);
+int gemm_bf16_pick_variant(double mean_rows_per_group);
+hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s);
+
+// fp32 vector-ALU GEMM (fp32 layers and the fp32 router contraction); M-tile height 64.
+constexpr int kF32TileM = 64;
+hipError_t launch_gemm_f32(const GemmCall& c, bool a_is_bf16, const float* col_bias,
+                           hipStream_t s);
+
+// Weighted combine (+ RMSNorm): out (T, K) D.
+hipError_t launch_combine(const Layer& ly, const void* y_assign, const float* w,
+                          const float* norm_weight, bool apply_norm, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,209 @@
+// Token counts per expert, expert offsets, the stable permutation of the token copies and
+// the per-expert M-tile list of the grouped GEMMs.
+//
+// "Как устроен Olmo-core 3: обучение больших MoE-моделей":
+//   * section "Балансировка нагрузки и вспомогательные штрафы": the selected indices are
+//     histogrammed over all tokens into one count per expert;
+//   * section "Пересылка токенов между экспертами": the expert indices are sorted, which
+//     orders the tokens by expert, and the bins are the cumulative sum of the counts;
+//   * section "Вычисления экспертов и точность": offsets are int32 cumulative sums.
+// The sort is stable over the flat assignment index a = t*k + j, so the permutation is
+// unique and identical on every run.
+//
+// Design (no sort, no order-dependent atomics):
+//   rank_kernel     256 tokens per block, one wavefront per 64 tokens. Each wavefront ORs
+//                   a bit per (expert, lane) into a 64-bit LDS mask (OR commutes, so the
+//                   masks are exact); a copy's rank inside the block is the popcount of the
+//                   lower lanes' bits plus the earlier wavefronts' counts. Block counts go
+//                   to an (E, nblocks) table.
+//   scan_cols       one block per expert: exclusive scan of its row of block counts ->
+//                   per-block bases; total -> counts[e].
+//   offsets_tiles   one block: exclusive scan of counts -> offsets; M-tiles per expert
+//                   (ceil(count / BM)) -> the tile list. Experts with no tokens get no tile,
+//                   so their weights are never read.
+//   permute         one thread per copy: position = offset + block base + rank.
+// Everything here moves O(T*k) int32 words: a few MB at the largest shapes.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRankTokens = 256;  // tokens per rank block (4 wavefronts)
+
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ idx, int64_t T, int k,
+                                                   int E, int nblk, int32_t* __restrict__ rank,
+                                                   int32_t* __restrict__ blk) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* bits = reinterpret_cast<uint64_t*>(smem);            // [4][E]
+  int32_t* pre = reinterpret_cast<int32_t*>(bits + 4 * E);       // [4][E]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x;
+  for (int e = lane; e < E; e += kWave) bits[wave * E + e] = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(b) * kRankTokens + wave * kWave + lane;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]),
+                                    1ull << lane);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      pre[w * E + e] = run;
+      run += __popcll(bits[w * E + e]);
+    }
+    blk[static_cast<int64_t>(e) * nblk + b] = run;
+  }
+  __syncthreads();
+  if (t < T) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e >= 0 && e < E)
+        rank[t * k + j] = pre[wave * E + e] + __popcll(bits[wave * E + e] & below);
+    }
+  }
+}
+
+// Inclusive scan across a 256- or 1024-thread block; `sh` holds one int per wavefront.
+__device__ int block_inclusive_scan(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == kWave - 1) sh[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int x = lane < nw ? sh[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_up(x, o, kWave);
+      if (lane >= o) x += u;
+    }
+    if (lane < nw) sh[lane] = x;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int add = wave > 0 ? sh[wave - 1] : 0;
+  const int total = sh[nw - 1];
+  __syncthreads();
+  sh[16] = total;  // published for the caller after the next barrier
+  return v + add;
+}
+
+__global__ __launch_bounds__(256) void scan_cols_kernel(int32_t* __restrict__ blk, int nblk,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int sh[17];
+  const int e = blockIdx.x;
+  int32_t* row = blk + static_cast<int64_t>(e) * nblk;
+  int carry = 0;
+  for (int base = 0; base < nblk; base += 256) {
+    const int i = base + threadIdx.x;
+    const int v = i < nblk ? row[i] : 0;
+    const int incl = block_inclusive_scan(v, sh);
+    if (i < nblk) row[i] = carry + incl - v;
+    __syncthreads();
+    carry += sh[16];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// counts -> offsets (or offsets given) -> M-tile list. One block of 1024 threads, E <= 1024.
+__global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __restrict__ counts_in,
+                                                             const int32_t* __restrict__ offsets_in,
+                                                             int32_t* __restrict__ offsets_out,
+                                                             int E, int bm, TileList tiles) {
+  __shared__ int sh[17];
+  const int e = threadIdx.x;
+  int c = 0, excl = 0;
+  if (offsets_in) {
+    if (e < E) {
+      excl = offsets_in[e];
+      c = offsets_in[e + 1] - excl;
+    }
+  } else {
+    c = e < E ? counts_in[e] : 0;
+    excl = block_inclusive_scan(c, sh) - c;
+    if (e < E) offsets_out[e] = excl;
+    if (e == E - 1) offsets_out[E] = excl + c;
+    __syncthreads();
+  }
+  if (tiles.cap <= 0) return;
+  c = c < 0 ? 0 : c;
+  const int mt = (c + bm - 1) / bm;
+  const int tbase = block_inclusive_scan(mt, sh) - mt;
+  __syncthreads();
+  const int total = sh[16];
+  for (int i = 0; i < mt; ++i) {
+    const int ti = tbase + i;
+    if (ti >= tiles.cap) break;
+    tiles.expert[ti] = e;
+    tiles.row0[ti] = excl + i * bm;
+    tiles.rows[ti] = min(bm, c - i * bm);
+  }
+  if (threadIdx.x == 0) *tiles.count = min(total, tiles.cap);
+}
+
+__global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ rank,
+                                                      const int32_t* __restrict__ blk, int nblk,
+                                                      const int32_t* __restrict__ offsets, int64_t A,
+                                                      int k, int E, int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ inv) {
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (a >= A) return;
+  const int e = idx[a];
+  if (e < 0 || e >= E) {
+    inv[a] = -1;
+    return;
+  }
+  const int64_t t = a / k;
+  const int64_t b = t / kRankTokens;
+  const int64_t pos = static_cast<int64_t>(offsets[e]) + blk[static_cast<int64_t>(e) * nblk + b] + rank[a];
+  if (pos >= 0 && pos < A) perm[pos] = static_cast<int32_t>(a);
+  inv[a] = static_cast<int32_t>(pos);
+}
+
+int num_rank_blocks(int64_t T) { return static_cast<int>((T + kRankTokens - 1) / kRankTokens); }
+
+}  // namespace
+
+size_t dispatch_scratch_bytes(const Layer& ly) {
+  const size_t A = static_cast<size_t>(ly.T) * ly.k;
+  const size_t nblk = static_cast<size_t>(num_rank_blocks(ly.T));
+  return (A + static_cast<size_t>(ly.E) * nblk) * sizeof(int32_t) + 256;
+}
+
+hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
+                           int bm, hipStream_t s) {
+  if (ly.T <= 0) return hipSuccess;
+  const int nblk = num_rank_blocks(ly.T);
+  const int64_t A = ly.T * ly.k;
+  int32_t* rank = static_cast<int32_t*>(scratch);
+  int32_t* blk = rank + A;
+  const size_t lds = static_cast<size_t>(ly.E) * 4 * (sizeof(uint64_t) + sizeof(int32_t));
+  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(256), lds, s, idx, ly.T, ly.k, ly.E, nblk, rank,
+                     blk);
+  hipLaunchKernelGGL(scan_cols_kernel, dim3(ly.E), dim3(256), 0, s, blk, nblk, counts);
+  hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, counts, nullptr, offsets, ly.E,
+                     bm, tiles);
+  hipLaunchKernelGGL(permute_kernel, dim3(static_cast<unsigned>((A + 255) / 256)), dim3(256), 0, s,
+                     idx, rank, blk, nblk, offsets, A, ly.k, ly.E, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
+                              int bm, hipStream_t s) {
+  hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, nullptr, offsets, nullptr,
+                     ly.E, bm, tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe
