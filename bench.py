@@ -31,11 +31,39 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also time each stage call alone")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times): the reference the HBM "
+                         "byte counters are scaled by")
     return ap.parse_args()
+
+
+def kernel_source_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "top_routing_grouped_router_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per expert-stage launch from the committed counter record (rocprofv3
+    FETCH_SIZE / WRITE_SIZE scaled by a copy calibration), or None when no record exists for
+    this workload or the kernel sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"expert_gemm_traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_sha256():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def event_time_ms(fn, n, torch):
@@ -78,10 +106,20 @@ def main():
         sys.exit(2)
     import torch
 
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
     import top_routing_grouped_router_amd as moe
     import workloads
 
-    torch.cuda.set_device(0)
     name = args.workload
     cfg, w, x = workloads.make_workload(name, device="cuda")
     T = x.shape[0]
@@ -132,7 +170,7 @@ def main():
         "layer_tflops": round(layer_flops / (ms / 1e3) / 1e12, 2),
         "roofline": {"kernel": "grouped expert GEMMs (up/gate+SwiGLU, down)", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(name),
                      "stage_ms": round(gemm_ms, 4), "flops_per_launch": gemm_flops},
     }
     if args.stages:

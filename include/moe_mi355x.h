@@ -181,7 +181,8 @@ MOE_API moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w
  * fp32; logits = x * router_weight^T (+ router_bias) in fp32; gating; top-k of the keys
  * (scores or logits, + score_bias); weights gathered / re-softmaxed, normalised and scaled.
  * Requires routing->expert_weights and routing->expert_indices; router_logits and
- * router_scores are filled when non-NULL. Uses the workspace for the logits otherwise.
+ * router_scores are filled when non-NULL. Uses the workspace (moe_workspace_size bytes) for
+ * partial sums of the logits.
  */
 MOE_API moe_status_t moe_router_forward(const moe_config_t* cfg, const moe_weights_t* weights,
                                 int64_t num_tokens, const void* x, moe_routing_t* routing,
@@ -207,7 +208,8 @@ MOE_API moe_status_t moe_route_from_scores(const moe_config_t* cfg, int64_t num_
  * distinct within a row (not checked on the device; out-of-range entries are not counted and
  * get no position). Outputs (all required): batch_size_per_expert (E), expert_offsets (E+1),
  * permutation (A), inverse_permutation (A); the permutation is the stable sort of t*k+j by
- * expert. Uses the workspace.
+ * expert. Uses the workspace. With T = 0 only the counts and offsets are written (zeros) and
+ * the other pointers may be NULL.
  */
 MOE_API moe_status_t moe_permute(const moe_config_t* cfg, int64_t num_tokens,
                          const int32_t* expert_indices, int32_t* batch_size_per_expert,

@@ -2,7 +2,14 @@
 
 Tolerances (stated once, used everywhere):
   * integer / index outputs: bit-exact;
-  * bf16 layers: max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_F / ||oracle||_F <= 1e-2;
+  * bf16 layers: ||gpu - oracle||_F / ||oracle||_F <= 1e-2 and max |gpu - oracle| <= 2e-2 on
+    every element but a tiny share (at most 1e-5 of the elements). Those few must be explained
+    by rounding the page fixes: the expert outputs Y are bf16 on both sides (the page on
+    grouped experts: they return bf16), computed from fp32 accumulation on the GPU and from
+    float64 in the oracle, so near a rounding boundary the two can land one bf16 spacing apart;
+    such a flip moves y by w * spacing(Y). The outlier bound is therefore 2e-2 + half the bf16
+    spacing of y (its own storage) + sum_j |w_j| * spacing(Y_j) (non-latent layers, where y is
+    the weighted sum itself);
   * fp32 layers: relative Frobenius <= 1e-5 and max |.| <= 1e-5 * max |oracle|;
   * fp32 routing weights: |gpu - oracle| <= 4e-6 * max(1, |oracle|) (a few fp32 roundings of
     the same fp32 inputs).
@@ -21,13 +28,14 @@ BF16_REL_FRO = 1e-2
 F32_REL_FRO = 1e-5
 F32_REL_MAX = 1e-5
 WEIGHT_TOL = 4e-6
+BF16_OUTLIER_SHARE = 1e-5
 
 
 def np32(t):
     return workloads.to_numpy_f32(t)
 
 
-def assert_close(got, ref, dtype: str, what: str = ""):
+def assert_close(got, ref, dtype: str, what: str = "", flip_allow=None):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -38,12 +46,37 @@ def assert_close(got, ref, dtype: str, what: str = ""):
     fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     mx = d.max()
     if dtype == "bf16":
-        assert mx <= BF16_MAX_ABS and fro <= BF16_REL_FRO, \
-            f"{what}: max-abs {mx:.3e} (<= {BF16_MAX_ABS}), rel-fro {fro:.3e} (<= {BF16_REL_FRO}), max|ref| {np.abs(ref).max():.3f}"
+        over = d > BF16_MAX_ABS
+        budget = max(1, int(BF16_OUTLIER_SHARE * d.size))
+        allowed = BF16_MAX_ABS + 0.5 * bf16_spacing(ref)
+        if flip_allow is not None:
+            allowed = allowed + np.asarray(flip_allow, np.float64)
+        msg = (f"{what}: max-abs {mx:.3e}, {int(over.sum())} elements above {BF16_MAX_ABS} (budget {budget}), "
+               f"worst excess over the rounding bound {float((d - allowed).max()):.3e}, rel-fro {fro:.3e} "
+               f"(<= {BF16_REL_FRO}), max|ref| {np.abs(ref).max():.3f}")
+        assert fro <= BF16_REL_FRO and int(over.sum()) <= budget and np.all(d <= allowed), msg
+        if over.any():
+            print(f"  note: {msg}")
     else:
         scale = np.abs(ref).max()
         assert fro <= F32_REL_FRO and mx <= F32_REL_MAX * max(scale, 1e-30), \
             f"{what}: rel-fro {fro:.3e} (<= {F32_REL_FRO}), max-abs {mx:.3e} (<= {F32_REL_MAX}*{scale:.3e})"
+
+
+def flip_allowance(cfgO, out):
+    """Per-element sum_j |w_j| * spacing(Y_j) for non-latent bf16 layers (else None)."""
+    if cfgO.latent_dim or cfgO.dtype != "bf16":
+        return None
+    w = np.asarray(out["w"], np.float64)
+    T, k = w.shape
+    Y = out["Y"][np.asarray(out["inv"]).reshape(T, k)]
+    return (np.abs(w)[:, :, None] * bf16_spacing(Y)).sum(axis=1)
+
+
+def bf16_spacing(a):
+    """Distance between consecutive bf16 numbers at |a| (8 significant bits)."""
+    a = np.maximum(np.abs(np.asarray(a, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
 
 
 def assert_weights_close(got, ref, what="weights"):

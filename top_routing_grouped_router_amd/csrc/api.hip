@@ -156,7 +156,7 @@ WsLayout ws_layout(const Layer& ly) {
   const size_t es = elem_size(ly);
   const int bm = expert_tile_m(ly);
   w.tile_cap = static_cast<int32_t>((A + bm - 1) / bm + E);
-  w.logits = c.take(T * E * 4);
+  w.logits = c.take(static_cast<size_t>(router_splits(ly)) * T * E * 4);  // logit partial sums
   w.idx = c.take(A * 4);
   w.w = c.take(A * 4);
   w.counts = c.take(E * 4);
@@ -376,7 +376,8 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
   hipStream_t s = static_cast<hipStream_t>(stream);
   moe_routing_t r{};
   if (routing) r = *routing;
-  float* logits = r.router_logits ? r.router_logits : at<float>(ws, L.logits);
+  float* parts = at<float>(ws, L.logits);
+  const int nsplit = router_splits(ly);
   int32_t* idx = r.expert_indices ? r.expert_indices : at<int32_t>(ws, L.idx);
   float* wts = r.expert_weights ? r.expert_weights : at<float>(ws, L.w);
   int32_t* counts = r.batch_size_per_expert ? r.batch_size_per_expert : at<int32_t>(ws, L.counts);
@@ -385,8 +386,10 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
   int32_t* inv = r.inverse_permutation ? r.inverse_permutation : at<int32_t>(ws, L.inv);
   const TileList tiles = tiles_of(ws, L);
 
-  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, w->router_bias, logits, s), "router logits");
-  MOE_TRY_HIP(launch_gate_topk(ly, logits, false, w->score_bias, idx, wts, r.router_scores, s), "gating/top-k");
+  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, s), "router logits");
+  MOE_TRY_HIP(launch_gate_topk(ly, parts, nsplit, false, w->score_bias, ly.router_bias ? w->router_bias : nullptr,
+                               idx, wts, r.router_scores, r.router_logits, s),
+              "gating/top-k");
   MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles,
                               expert_tile_m(ly), s),
               "dispatch");
@@ -419,19 +422,18 @@ moe_status_t moe_router_forward(const moe_config_t* c, const moe_weights_t* w, i
   if ((st = need(routing->expert_weights, "routing->expert_weights")) != MOE_OK) return st;
   if (T == 0) return ok();
   if ((st = need(x, "x")) != MOE_OK) return st;
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
   const Layer ly = make_layer(c, T);
-  float* logits = routing->router_logits;
-  if (!logits) {
-    if ((st = need(ws, "workspace (needed when routing->router_logits is NULL)")) != MOE_OK) return st;
-    const WsLayout L = ws_layout(ly);
-    if (ws_bytes < L.logits + static_cast<size_t>(T) * ly.E * 4)
-      return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the router logits");
-    logits = at<float>(ws, L.logits);
-  }
+  const WsLayout L = ws_layout(ly);
+  const int nsplit = router_splits(ly);
+  if (ws_bytes < L.logits + static_cast<size_t>(nsplit) * T * ly.E * 4)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the router partial sums");
+  float* parts = at<float>(ws, L.logits);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, w->router_bias, logits, s), "router logits");
-  MOE_TRY_HIP(launch_gate_topk(ly, logits, false, w->score_bias, routing->expert_indices, routing->expert_weights,
-                               routing->router_scores, s),
+  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, s), "router logits");
+  MOE_TRY_HIP(launch_gate_topk(ly, parts, nsplit, false, w->score_bias, ly.router_bias ? w->router_bias : nullptr,
+                               routing->expert_indices, routing->expert_weights, routing->router_scores,
+                               routing->router_logits, s),
               "gating/top-k");
   return ok();
 }
@@ -447,8 +449,8 @@ moe_status_t moe_route_from_scores(const moe_config_t* c, int64_t T, const float
   if (T == 0) return ok();
   if ((st = need(sel_input, "sel_input")) != MOE_OK) return st;
   const Layer ly = make_layer(c, T);
-  MOE_TRY_HIP(launch_gate_topk(ly, sel_input, true, score_bias, expert_indices, expert_weights, nullptr,
-                               static_cast<hipStream_t>(stream)),
+  MOE_TRY_HIP(launch_gate_topk(ly, sel_input, 1, true, score_bias, nullptr, expert_indices, expert_weights,
+                               nullptr, nullptr, static_cast<hipStream_t>(stream)),
               "route from scores");
   return ok();
 }
@@ -460,18 +462,18 @@ moe_status_t moe_permute(const moe_config_t* c, int64_t T, const int32_t* idx, i
   if ((st = check_tokens(c, T)) != MOE_OK) return st;
   if ((st = need(counts, "batch_size_per_expert")) != MOE_OK) return st;
   if ((st = need(offsets, "expert_offsets")) != MOE_OK) return st;
-  if ((st = need(perm, "permutation")) != MOE_OK) return st;
-  if ((st = need(inv, "inverse_permutation")) != MOE_OK) return st;
-  if ((st = need(ws, "workspace")) != MOE_OK) return st;
   const Layer ly = make_layer(c, T);
-  const WsLayout L = ws_layout(ly);
-  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (T == 0) {
+  if (T == 0) {  // no assignments: permutation buffers are empty (may be NULL)
     MOE_TRY_HIP(hipMemsetAsync(counts, 0, sizeof(int32_t) * ly.E, s), "zero counts");
     MOE_TRY_HIP(hipMemsetAsync(offsets, 0, sizeof(int32_t) * (ly.E + 1), s), "zero offsets");
     return ok();
   }
+  if ((st = need(perm, "permutation")) != MOE_OK) return st;
+  if ((st = need(inv, "inverse_permutation")) != MOE_OK) return st;
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
+  const WsLayout L = ws_layout(ly);
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   if ((st = need(idx, "expert_indices")) != MOE_OK) return st;
   MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles_of(ws, L),
                               expert_tile_m(ly), s),

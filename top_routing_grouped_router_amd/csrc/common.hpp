@@ -98,15 +98,18 @@ int device_cu_count();
 // ---------------------------------------------------------------- launchers (host)
 // Every launcher enqueues on `s` and returns hipSuccess or the launch error.
 
-// Router logits: logits (T,E) f32 = x (T,d) * Wr^T (+ bias). x is f32 or bf16 bits.
-hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, const float* br,
-                                float* logits, hipStream_t s);
+// Router logits as nsplit partial-sum planes (nsplit, T, E) f32 of x (T,d) * Wr^T; the gate
+// kernel adds the planes (fixed order) and the router bias. x is f32 or bf16 bits.
+int router_splits(const Layer& ly);
+hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, float* partials,
+                                int nsplit, hipStream_t s);
 
-// Gating + top-k + weights from logits (from_scores = false) or from the gating output
-// (from_scores = true: scores for softmax/sigmoid, logits for topk_softmax).
-hipError_t launch_gate_topk(const Layer& ly, const float* input, bool from_scores,
-                            const float* score_bias, int32_t* idx, float* w, float* scores_out,
-                            hipStream_t s);
+// Gating + top-k + weights from logit partials (from_scores = false) or from the gating output
+// (from_scores = true: scores for softmax/sigmoid, logits for topk_softmax; nsplit ignored).
+// logits_out / scores_out (T, E) are optional diagnostics.
+hipError_t launch_gate_topk(const Layer& ly, const float* input, int nsplit, bool from_scores,
+                            const float* score_bias, const float* router_bias, int32_t* idx, float* w,
+                            float* scores_out, float* logits_out, hipStream_t s);
 
 // Histogram, stable permutation and the M-tile list (tile height bm).
 size_t dispatch_scratch_bytes(const Layer& ly);

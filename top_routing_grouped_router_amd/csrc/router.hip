@@ -14,8 +14,17 @@
 // логитов и квантизация"); keys compare as IEEE numbers (-0.0 == +0.0) and NaN keys rank
 // after every number.
 //
+// router_mfma: the fp32 contraction on bf16 matrix cores. Each fp32 router weight is split
+// exactly into three bf16 planes (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid):
+// 24 significant bits between them); x is bf16, so every product x * plane is exact in fp32
+// and the three MFMA products accumulate in fp32 -- an fp32-accurate dot product (3*d terms)
+// at bf16 matrix rate. Tile 64 tokens x 64 experts x 64 k, four wavefronts of 32 x 32 on
+// v_mfma_f32_16x16x32_bf16. The contraction can be split over `nsplit` workgroups along
+// d_model for occupancy; the partial sums land in separate planes and the gate kernel adds
+// them in a fixed order, so the result is deterministic.
+//
 // gate_topk: one 64-lane wavefront per token; each lane holds ceil(E/64) <= 16 experts in
-// registers. Selection is k rounds of a wave-wide arg-max over a 64-bit key
+// registers (the count is a template parameter). Selection is k rounds of a wave-wide arg-max over a 64-bit key
 // (order-preserving bits of the key, then the complemented expert index), so each round is
 // six xor-shuffle steps and the result is exact and deterministic. The logits row is read
 // once, coalesced; the kernel is bound by HBM/L2 reads of the logits.
@@ -26,7 +35,7 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxPerLane = MOE_MAX_EXPERTS / kWave;  // 16
+constexpr int kMaxSlots = MOE_MAX_EXPERTS / kWave;  // 16 experts per lane at most
 
 // Order-preserving 32-bit code of a selection key: larger key -> larger code; both zeros map
 // to one code; NaN maps to 1, below every number (-inf maps to 0x007FFFFF); 0 means "no
@@ -39,7 +48,10 @@ __device__ __forceinline__ uint32_t key_code(float key) {
 }
 
 struct GateArgs {
-  const float* in;          // (T, E) logits, or the gating output when from_scores
+  const float* in;          // (nsplit, T, E) logit partial sums, or (T, E) gating output
+  int nsplit;               // partial-sum planes to add (1 when from_scores)
+  const float* router_bias; // (E) or NULL, added to the logits
+  float* logits_out;        // (T, E) or NULL
   const float* score_bias;  // (E) or NULL
   int32_t* idx;             // (T, k)
   float* w;                 // (T, k)
@@ -54,20 +66,30 @@ struct GateArgs {
   int orig_k;
 };
 
-template <int GATING, bool FROM_SCORES>
+template <int GATING, bool FROM_SCORES, int PL>
 __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
+  constexpr int kMaxPerLane = PL;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;  // whole wavefront leaves together
   const int E = a.E;
+  const int64_t plane = a.T * static_cast<int64_t>(E);
   const float* row = a.in + t * E;
 
-  float v[kMaxPerLane];  // input values
+  float v[kMaxPerLane];  // logits (or the given gating output)
   float s[kMaxPerLane];  // gating scores (unused for topk_softmax weights)
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = i * kWave + lane;
-    v[i] = (i * kWave < E && e < E) ? row[e] : -INFINITY;
+    if (e < E) {
+      float acc = row[e];
+      for (int p = 1; p < a.nsplit; ++p) acc += row[p * plane + e];
+      if (!FROM_SCORES && a.router_bias) acc += a.router_bias[e];
+      v[i] = acc;
+      if (!FROM_SCORES && a.logits_out) a.logits_out[t * E + e] = acc;
+    } else {
+      v[i] = -INFINITY;
+    }
   }
 
   if (!FROM_SCORES) {
@@ -98,7 +120,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = i * kWave + lane;
-        if (i * kWave < E && e < E) a.scores_out[t * E + e] = s[i];
+        if (e < E) a.scores_out[t * E + e] = s[i];
       }
     }
   } else {
@@ -111,7 +133,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = i * kWave + lane;
-    if (i * kWave < E && e < E) {
+    if (e < E) {
       float key = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[i] : s[i];
       if (a.score_bias) key = key + a.score_bias[e];
       cand[i] = (static_cast<uint64_t>(key_code(key)) << 32) | static_cast<uint32_t>(~e);
@@ -140,7 +162,15 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   const bool active = lane < a.k;
   float w;
   if (GATING == MOE_GATING_TOPK_SOFTMAX) {
-    const float lv = active ? row[my_sel] : -INFINITY;
+    // the selected expert's logit, from the register of its owning lane
+    const int src = my_sel & (kWave - 1), slot = my_sel >> 6;
+    float lv = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const float sv = __shfl(v[i], src, kWave);
+      if (i == slot) lv = sv;
+    }
+    if (!active) lv = -INFINITY;
     const float m = wave_max(lv);
     const float ex = active ? expf(lv - m) : 0.f;
     const float sum = wave_sum(ex);
@@ -178,21 +208,193 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   }
 }
 
+template <int GATING, bool FS>
+void launch_gate_pl(const GateArgs& a, hipStream_t s) {
+  const dim3 g(static_cast<unsigned>((a.T + 3) / 4)), b(256);
+  const int per_lane = (a.E + kWave - 1) / kWave;
+  if (per_lane <= 1) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 1>), g, b, 0, s, a);
+  else if (per_lane <= 2) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 2>), g, b, 0, s, a);
+  else if (per_lane <= 4) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 4>), g, b, 0, s, a);
+  else if (per_lane <= 8) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 8>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, kMaxSlots>), g, b, 0, s, a);
+}
+
 template <int GATING>
 void launch_gate(const GateArgs& a, bool from_scores, hipStream_t s) {
-  const dim3 g(static_cast<unsigned>((a.T + 3) / 4)), b(256);
-  if (from_scores) hipLaunchKernelGGL((gate_topk_kernel<GATING, true>), g, b, 0, s, a);
-  else hipLaunchKernelGGL((gate_topk_kernel<GATING, false>), g, b, 0, s, a);
+  if (from_scores) launch_gate_pl<GATING, true>(a, s);
+  else launch_gate_pl<GATING, false>(a, s);
+}
+
+// ------------------------------------------------------------------ router logits on MFMA
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRT = 64;    // tokens per tile
+constexpr int kRE = 64;    // experts per tile
+constexpr int kRBK = 64;   // k per stage
+constexpr int kRowB = kRBK * 2;
+constexpr int kXBytes = kRT * kRowB;        // 8 KiB
+constexpr int kPlaneBytes = kRE * kRowB;    // 8 KiB per bf16 plane
+constexpr int kRStage = kXBytes + 3 * kPlaneBytes;
+
+__device__ __forceinline__ int rswz(int row, int chunk) {
+  return row * kRowB + ((chunk ^ (row & 7)) << 4);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
+  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ Wr,
+                                                          float* __restrict__ part, int64_t T, int E,
+                                                          int d, int nsplit) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kRStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 wavefronts of 32 tokens x 32 experts
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRT;
+  const int e0 = blockIdx.y * kRE;
+  const int sp = blockIdx.z;
+  const int nk = d / kRBK;
+  const int kb = static_cast<int>(static_cast<int64_t>(sp) * nk / nsplit);
+  const int ke = static_cast<int>(static_cast<int64_t>(sp + 1) * nk / nsplit);
+
+  const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
+  const unsigned char* wb = reinterpret_cast<const unsigned char*>(Wr);
+  uint32_t xoff[2], woff[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = tid + 256 * q, row = c >> 3, ch = c & 7;
+    const int64_t t = min(t0 + row, T - 1);
+    xoff[q] = static_cast<uint32_t>((t * d + ch * 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = tid + 256 * q, row = c >> 4, c4 = c & 15;
+    const int64_t e = min(e0 + row, E - 1);
+    woff[q] = static_cast<uint32_t>((e * d + c4 * 4) * 4);
+  }
+
+  u32x4 rx[2];
+  f32x4 rw[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      rx[q] = *reinterpret_cast<const u32x4*>(xb + (xoff[q] + static_cast<uint32_t>(kt) * kRowB));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      rw[q] = *reinterpret_cast<const f32x4*>(wb + (woff[q] + static_cast<uint32_t>(kt) * (kRBK * 4)));
+  };
+  auto sstore = [&](int buf) {
+    unsigned char* base = lds + buf * kRStage;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = tid + 256 * q;
+      *reinterpret_cast<u32x4*>(base + rswz(c >> 3, c & 7)) = rx[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q, row = c >> 4, c4 = c & 15;
+      uint16_t hi[4], mi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float w = rw[q][r];
+        hi[r] = f32_to_bf16_bits(w);
+        const float r1 = w - bf16_bits_to_f32(hi[r]);
+        mi[r] = f32_to_bf16_bits(r1);
+        const float r2 = r1 - bf16_bits_to_f32(mi[r]);
+        lo[r] = f32_to_bf16_bits(r2);
+      }
+      const int off = rswz(row, c4 >> 1) + (c4 & 1) * 8;
+      unsigned char* pl = base + kXBytes;
+      *reinterpret_cast<uint2*>(pl + off) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+      *reinterpret_cast<uint2*>(pl + kPlaneBytes + off) = make_uint2(pack2(mi[0], mi[1]), pack2(mi[2], mi[3]));
+      *reinterpret_cast<uint2*>(pl + 2 * kPlaneBytes + off) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+    }
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (kb < ke) {
+    gload(kb);
+    sstore(0);
+    __syncthreads();
+    for (int kt = kb; kt < ke; ++kt) {
+      const int buf = (kt - kb) & 1;
+      if (kt + 1 < ke) gload(kt + 1);
+      const unsigned char* X = lds + buf * kRStage;
+      const unsigned char* Wp = X + kXBytes;
+#pragma unroll
+      for (int s32 = 0; s32 < 2; ++s32) {
+        const int ch = 4 * s32 + (lane >> 4);
+        bf16x8 xf[2], wf[3][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          xf[i] = *reinterpret_cast<const bf16x8*>(X + rswz(32 * wm + 16 * i + (lane & 15), ch));
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            wf[p][j] = *reinterpret_cast<const bf16x8*>(Wp + p * kPlaneBytes +
+                                                       rswz(32 * wn + 16 * j + (lane & 15), ch));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int p = 2; p >= 0; --p)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[p][j], xf[i], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < ke) sstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Lane holds token (lane & 15) of each 16-token sub-tile and experts 4*(lane >> 4) + r.
+  float* out = part + static_cast<int64_t>(sp) * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = t0 + 32 * wm + 16 * i + (lane & 15);
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 32 * wn + 16 * j + 4 * (lane >> 4) + r;
+        if (e < E) out[t * E + e] = acc[i][j][r];
+      }
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gate_topk(const Layer& ly, const float* input, bool from_scores,
-                            const float* score_bias, int32_t* idx, float* w, float* scores_out,
-                            hipStream_t s) {
+int router_splits(const Layer& ly) {
+  if (!ly.bf16) return 1;
+  const int64_t tiles = ((ly.T + kRT - 1) / kRT) * ((ly.E + kRE - 1) / kRE);
+  const int nk = static_cast<int>(ly.d / kRBK);
+  int s = 1;
+  // enough workgroups to cover the chip (a fixed target, so the workspace size does not
+  // depend on the device), each keeping at least one k-stage
+  while (s * 2 <= nk && s < 32 && tiles * s < 512) s *= 2;
+  return s;
+}
+
+hipError_t launch_gate_topk(const Layer& ly, const float* input, int nsplit, bool from_scores,
+                            const float* score_bias, const float* router_bias, int32_t* idx, float* w,
+                            float* scores_out, float* logits_out, hipStream_t s) {
   if (ly.T <= 0) return hipSuccess;
   GateArgs a;
   a.in = input;
+  a.nsplit = from_scores ? 1 : nsplit;
+  a.router_bias = from_scores ? nullptr : router_bias;
+  a.logits_out = from_scores ? nullptr : logits_out;
   a.score_bias = score_bias;
   a.idx = idx;
   a.w = w;
@@ -213,15 +415,22 @@ hipError_t launch_gate_topk(const Layer& ly, const float* input, bool from_score
   return hipGetLastError();
 }
 
-hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, const float* br,
-                                float* logits, hipStream_t s) {
+hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, float* partials,
+                                int nsplit, hipStream_t s) {
   if (ly.T <= 0) return hipSuccess;
+  if (ly.bf16) {
+    const dim3 g(static_cast<unsigned>((ly.T + kRT - 1) / kRT), static_cast<unsigned>((ly.E + kRE - 1) / kRE),
+                 static_cast<unsigned>(nsplit));
+    hipLaunchKernelGGL(router_mfma_kernel, g, dim3(256), 0, s, static_cast<const uint16_t*>(x), Wr, partials,
+                       ly.T, ly.E, static_cast<int>(ly.d), nsplit);
+    return hipGetLastError();
+  }
   GemmCall c{};
   c.A = x;
   c.lda = ly.d;
   c.B = Wr;
   c.ldb = ly.d;
-  c.C = logits;
+  c.C = partials;
   c.ldc = ly.E;
   c.N = ly.E;
   c.Kd = ly.d;
@@ -229,7 +438,7 @@ hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr,
   c.a_rows = ly.T;
   c.c_rows = ly.T;
   c.rows_bound = ly.T;
-  return launch_gemm_f32(c, ly.bf16, ly.router_bias ? br : nullptr, s);
+  return launch_gemm_f32(c, false, nullptr, s);
 }
 
 }  // namespace moe
