@@ -18,7 +18,7 @@
 //   * Tile = (WM*TM*32 token rows) x (WN*TN*32 weight rows) x 64 k, 4 wavefronts. The large
 //     variant is 256 x 256 (each wavefront 128 x 128: 16 MFMA accumulators of 16 floats).
 //     LDS holds two stages of both tiles (128 KiB for 256 x 256); 16-byte chunks are XOR-
-//     swizzled by row so the per-lane 16-byte fragment reads hit distinct banks.
+//     swizzled by row pair so fragment reads and staging writes are free of bank conflicts.
 //   * The A loader gathers token rows through the permutation (row = perm[p] / k), so the
 //     permuted copy of the tokens is never materialised; the GEMM2 epilogue scatters rows to
 //     assignment order, so the combine reads each token's k rows contiguously.
@@ -34,42 +34,108 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;         // k per stage
-constexpr int ROWB = BK * 2;   // bytes per staged row
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 
-template <int WM_, int WN_, int TM_, int TN_>
+template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_>
 struct Shape {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
-  static constexpr int NT = WM * WN * kWave;  // threads
-  static constexpr int BM = WM * TM * 32;     // token rows
-  static constexpr int BN = WN * TN * 32;     // weight rows
-  static constexpr int RPP = NT / 8;          // rows staged per pass (8 chunks per row)
-  static constexpr int A_CH = BM / RPP;       // 16-byte chunks per thread per stage
-  static constexpr int B_CH = BN / RPP;
+  static constexpr int BK = BK_;                // k per pipeline stage
+  static constexpr int ROWB = BK * 2;           // bytes per staged row
+  static constexpr int CHUNKS = ROWB / 16;      // 16-byte chunks per staged row
+  static constexpr int ROWS_PER_BANKLINE = 256 / ROWB;  // rows sharing the 64 LDS banks
+  static constexpr int kRowsPerDma = 1024 / ROWB;       // rows one wave-wide 16-byte DMA load fills
+  static constexpr int NSTAGE = NSTAGE_;        // LDS ring depth; loads run NSTAGE-1 stages ahead
+  static constexpr int WG_PER_CU = WG_PER_CU_;  // resident workgroups per CU (persistent grid)
+  static constexpr int NW = WM * WN;            // wavefronts
+  static constexpr int NT = NW * kWave;         // threads
+  static constexpr int BM = WM * TM * 32;       // token rows
+  static constexpr int BN = WN * TN * 32;       // weight rows
+  static constexpr int NI = (BM + BN) / kRowsPerDma;   // DMA loads per stage
+  static constexpr int NQ = (NI + NW - 1) / NW;        // per wavefront (upper bound)
+  static constexpr int NQMIN = NI / NW;                // per wavefront (lower bound)
   static constexpr int STAGE = (BM + BN) * ROWB;
-  static_assert(BM % RPP == 0 && BN % RPP == 0, "whole chunks per thread");
+  static constexpr int LDS = NSTAGE * STAGE;
+  static_assert(BM % kRowsPerDma == 0 && BN % kRowsPerDma == 0, "whole DMA loads per tile");
+  static_assert(BK % 16 == 0 && CHUNKS >= 2 && CHUNKS <= 8, "stage depth");
   static_assert(TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "vmcnt bookkeeping covers 2..4 stages");
+  static_assert(LDS * WG_PER_CU <= 160 * 1024, "LDS budget");
 };
 
-// 256 x 256 tile, 8 wavefronts (2 x 4), each 128 token rows x 64 weight rows.
-using ShapeLarge = Shape<2, 4, 4, 2>;
-// 32 x 256 tile, 4 wavefronts (1 x 4): few rows per expert (decode-shaped loads).
-using ShapeSmall = Shape<1, 4, 1, 2>;
+// The load path (texture addresser / L1, 128-byte lines) is the scarce resource of these GEMMs,
+// more than the matrix pipes: every staged row is one whole 128-byte line (k-stage 64), and
+// tiles are as large as LDS allows so each line feeds as many MFMAs as possible.
+// 256 x 256 tile, 8 wavefronts (2 x 4) of 128 token rows x 64 weight rows; 2 stages x 64 KiB.
+using ShapeLarge = Shape<2, 4, 4, 2, 64, 2, 1>;
+// 64 x 256 tile, 4 wavefronts (1 x 4) of 64 x 64: few rows per expert (decode-shaped loads);
+// 2 stages x 40 KiB, two workgroups per CU.
+using ShapeSmall = Shape<1, 4, 2, 2, 64, 2, 2>;
 
+// LDS is 64 banks of 4 bytes and a 16-byte access serves 16 lanes per pass. A staged row covers
+// 1/ROWS_PER_BANKLINE of the banks; chunk c of row r lives in slot c ^ ((r / ROWS_PER_BANKLINE)
+// & (CHUNKS - 1)), so the 16 consecutive rows of one fragment read (same chunk) hit 16 distinct
+// 16-byte bank groups. DMA writes are linear in the lane index: conflict-free by construction.
+template <class S>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * ROWB + ((chunk ^ (row & 7)) << 4);
+  return row * S::ROWB + ((chunk ^ ((row / S::ROWS_PER_BANKLINE) & (S::CHUNKS - 1))) << 4);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Instruction-scheduling directives for one pipeline stage: step 0's LDS reads first, then in
+// each k16 step pair MFMAs with the next step's LDS reads and with this stage's share of the
+// global->LDS loads, so neither the LDS round trip nor the address unit stalls the matrix pipe.
+// (Masks: 0x008 MFMA, 0x010 VMEM, 0x100 DS read.)
+template <int KK, int KSTEPS, int KREADS, int KMFMA, int KLOADS, int LEFT>
+__device__ __forceinline__ void sched_stage_step() {
+  if constexpr (KK < KSTEPS) {
+    constexpr int reads = (KK + 1 < KSTEPS) ? KREADS : 0;
+    constexpr int per = (KLOADS + KSTEPS - 1) / KSTEPS;
+    constexpr int loads = LEFT < per ? LEFT : per;
+    constexpr int r1 = reads < KMFMA ? reads : KMFMA;
+    constexpr int l1 = loads < (KMFMA - r1) ? loads : (KMFMA - r1);
+#pragma unroll
+    for (int q = 0; q < r1; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (reads > r1) __builtin_amdgcn_sched_group_barrier(0x100, reads - r1, 0);
+#pragma unroll
+    for (int q = 0; q < l1; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    }
+    if constexpr (loads > l1) __builtin_amdgcn_sched_group_barrier(0x010, loads - l1, 0);
+    if constexpr (KMFMA - r1 - l1 > 0) __builtin_amdgcn_sched_group_barrier(0x008, KMFMA - r1 - l1, 0);
+    sched_stage_step<KK + 1, KSTEPS, KREADS, KMFMA, KLOADS, LEFT - loads>();
+  }
+}
+
+template <int KSTEPS, int KREADS, int KMFMA, int KLOADS>
+__device__ __forceinline__ void sched_stage() {
+  __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);  // step-0 reads
+  sched_stage_step<0, KSTEPS, KREADS, KMFMA, KLOADS, KLOADS>();
 }
 
 template <class S, bool SWIGLU, bool GATHER, bool SCATTER>
-__global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * S::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[S::LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wavefront coordinates are uniform per wavefront: keep them in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WN, wn = wave % S::WN;
-  const int ld_chunk = tid & 7, ld_row = tid >> 3;  // RPP rows per pass
 
   const int64_t cols_per_tile = SWIGLU ? S::BN / 2 : S::BN;
   const int64_t ntn = (c.N + cols_per_tile - 1) / cols_per_tile;
@@ -81,9 +147,13 @@ __global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
   const int per_xcd = gridDim.x / kXcds;
   const int slot = blockIdx.x / kXcds;
   const int64_t chunk = (total + kXcds - 1) / kXcds;
-  const int nk = static_cast<int>(c.Kd / BK);
-  const uint16_t* Abase = static_cast<const uint16_t*>(c.A);
+  const int nk = static_cast<int>(c.Kd / S::BK);
+  const unsigned char* Ab = static_cast<const unsigned char*>(c.A);
   uint16_t* Cbase = static_cast<uint16_t*>(c.C);
+
+  // this lane's row inside a DMA load, and the logical 16-byte chunk it fetches so that the
+  // linear LDS write lands in the swizzled slot
+  const int dma_row = lane / S::CHUNKS;
 
   for (int64_t it = slot; it < chunk; it += per_xcd) {
     const int64_t lin = xcd * chunk + it;
@@ -106,38 +176,54 @@ __global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
       rows = c.tiles.rows[mt];
       grp = c.tiles.expert[mt];
     }
-
-    // Per-thread 32-bit byte offsets of the rows this thread stages (uniform bases stay in
-    // scalar registers; the loads use the scalar-base + vector-offset form).
-    uint32_t a_off[S::A_CH];
-#pragma unroll
-    for (int q = 0; q < S::A_CH; ++q) {
-      const int r = ld_row + S::RPP * q;
-      int64_t p = row0 + (r < rows ? r : 0);
-      p = min(max(p, int64_t(0)), c.rows_bound - 1);
-      int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
-      src = min(max(src, int64_t(0)), c.a_rows - 1);
-      a_off[q] = static_cast<uint32_t>((src * c.lda + ld_chunk * 8) * 2);
-    }
     const unsigned char* Bexp =
         reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(c.B) + grp * c.b_group_stride);
-    uint32_t b_off[S::B_CH];
+
+    // Per DMA load q of this wavefront: 32-bit byte offset of the source 16-byte chunk (stage 0)
+    // and whether it reads the token (A) or weight (B) operand.
+    uint32_t src_off[S::NQ];
+    bool is_a[S::NQ];
 #pragma unroll
-    for (int q = 0; q < S::B_CH; ++q) {
-      const int r = ld_row + S::RPP * q;
-      int64_t wrow;
-      if (SWIGLU) {
-        const int wv = r / (S::TN * 32), qq = r % (S::TN * 32);
-        const int half = qq / (S::TN * 16);
-        int64_t col = nt * (S::BN / 2) + wv * (S::TN * 16) + (qq % (S::TN * 16));
-        col = min(col, c.N - 1);
-        wrow = col + (half ? c.swiglu_h : 0);
+    for (int q = 0; q < S::NQ; ++q) {
+      const int i = wave + S::NW * q;  // load index inside the stage (uniform)
+      is_a[q] = i < S::BM / S::kRowsPerDma;
+      const int r = (is_a[q] ? i : i - S::BM / S::kRowsPerDma) * S::kRowsPerDma + dma_row;
+      const int chunk_l = (lane % S::CHUNKS) ^ ((r / S::ROWS_PER_BANKLINE) & (S::CHUNKS - 1));
+      if (is_a[q]) {
+        int64_t p = row0 + (r < rows ? r : 0);
+        p = min(max(p, int64_t(0)), c.rows_bound - 1);
+        int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
+        src = min(max(src, int64_t(0)), c.a_rows - 1);
+        src_off[q] = static_cast<uint32_t>(src * c.lda * 2 + chunk_l * 16);
       } else {
-        wrow = min(nt * S::BN + r, c.N - 1);
+        int64_t wrow;
+        if (SWIGLU) {
+          const int wv = r / (S::TN * 32), qq = r % (S::TN * 32);
+          const int half = qq / (S::TN * 16);
+          int64_t col = nt * (S::BN / 2) + wv * (S::TN * 16) + (qq % (S::TN * 16));
+          col = min(col, c.N - 1);
+          wrow = col + (half ? c.swiglu_h : 0);
+        } else {
+          wrow = min(nt * S::BN + r, c.N - 1);
+        }
+        src_off[q] = static_cast<uint32_t>(wrow * c.ldb * 2 + chunk_l * 16);
       }
-      b_off[q] = static_cast<uint32_t>((wrow * c.ldb + ld_chunk * 8) * 2);
     }
-    const unsigned char* Ab = reinterpret_cast<const unsigned char*>(Abase);
+
+    // Issue the DMA loads of pipeline stage kt into ring slot kt % NSTAGE.
+    // Issue loads q in [q0, q1) of pipeline stage kt into ring slot `ring_slot`.
+    auto issue_part = [&](int kt, int ring_slot, int q0, int q1) {
+      unsigned char* st = lds + ring_slot * S::STAGE;
+#pragma unroll
+      for (int q = 0; q < S::NQ; ++q) {
+        if (q < q0 || q >= q1) continue;
+        const int i = wave + S::NW * q;
+        if (S::NI % S::NW != 0 && i >= S::NI) continue;
+        const unsigned char* g = (is_a[q] ? Ab : Bexp) + (src_off[q] + static_cast<uint32_t>(kt) * S::ROWB);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
+      }
+    };
+    auto issue = [&](int kt, int ring_slot) { issue_part(kt, ring_slot, 0, S::NQ); };
 
     f32x16 acc[S::TM][S::TN];
 #pragma unroll
@@ -147,53 +233,69 @@ __global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 ra[S::A_CH], rb[S::B_CH];
-    auto gload = [&](int kt) {
+    bf16x8 fw[2][S::TN], ft[2][S::TM];
+    auto lds_frags = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
+      const int ch = 2 * kk + (lane >> 5);
 #pragma unroll
-      for (int q = 0; q < S::A_CH; ++q)
-        ra[q] = *reinterpret_cast<const u32x4*>(Ab + (a_off[q] + static_cast<uint32_t>(kt) * ROWB));
+      for (int j = 0; j < S::TN; ++j)
+        fw[fs][j] = *reinterpret_cast<const bf16x8*>(lb + swz<S>(wn * S::TN * 32 + j * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int q = 0; q < S::B_CH; ++q)
-        rb[q] = *reinterpret_cast<const u32x4*>(Bexp + (b_off[q] + static_cast<uint32_t>(kt) * ROWB));
-    };
-    auto sstore = [&](int buf) {
-      unsigned char* la = lds + buf * S::STAGE;
-      unsigned char* lb = la + S::BM * ROWB;
-#pragma unroll
-      for (int q = 0; q < S::A_CH; ++q)
-        *reinterpret_cast<u32x4*>(la + swz(ld_row + S::RPP * q, ld_chunk)) = ra[q];
-#pragma unroll
-      for (int q = 0; q < S::B_CH; ++q)
-        *reinterpret_cast<u32x4*>(lb + swz(ld_row + S::RPP * q, ld_chunk)) = rb[q];
+      for (int i = 0; i < S::TM; ++i)
+        ft[fs][i] = *reinterpret_cast<const bf16x8*>(la + swz<S>(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    // Output rows of this lane's token sub-tiles. The scatter indices are loaded now and only
+    // used (clamped) in the epilogue, so their latency hides under the k-loop.
+    int64_t out_row[S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) {
+      const int m = wm * S::TM * 32 + i * 32 + (lane & 31);
+      const int64_t p = min(row0 + (m < rows ? m : 0), c.rows_bound - 1);
+      out_row[i] = SCATTER ? static_cast<int64_t>(c.scatter[p]) : p;
+    }
+
+    // Prologue: NSTAGE-1 stages in flight.
+#pragma unroll
+    for (int s0 = 0; s0 < S::NSTAGE - 1; ++s0)
+      issue(min(s0, nk - 1), s0);
+
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const unsigned char* la = lds + buf * S::STAGE;
-      const unsigned char* lb = la + S::BM * ROWB;
+      // Wait until this wavefront's loads of stage kt have landed (younger stages may stay in
+      // flight), then a barrier: every wavefront's part of stage kt is in LDS, and every
+      // wavefront has finished reading stage kt-1, whose ring slot is refilled below.
+      const int younger = min(S::NSTAGE - 2, nk - 1 - kt);
+      if (younger >= 2) wait_vmcnt<2 * S::NQMIN>();
+      else if (younger == 1) wait_vmcnt<S::NQMIN>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+
+      const unsigned char* la = lds + (kt % S::NSTAGE) * S::STAGE;
+      const unsigned char* lb = la + S::BM * S::ROWB;
+      // Refill the ring slot freed by the barrier: stage kt+NSTAGE-1 lands while this stage
+      // computes. Past the last stage the issue is clamped to re-fetch the last stage into the
+      // idle slot (never read), which keeps the loop branch-free.
+      issue(min(kt + S::NSTAGE - 1, nk - 1), (kt + S::NSTAGE - 1) % S::NSTAGE);
+      // k16 steps with fragments double-buffered in registers; the directives interleave step
+      // kk+1's LDS reads with step kk's MFMAs so the matrix pipe does not wait on an LDS round
+      // trip before every MFMA group.
+      constexpr int kSteps = S::BK / 16;
+      constexpr int kReads = S::TM + S::TN;   // LDS fragment reads per k16 step
+      constexpr int kMfma = S::TM * S::TN;    // MFMAs per k16 step
+      lds_frags(0, la, lb, 0);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int ch = 2 * kk + (lane >> 5);
-        bf16x8 fw[S::TN], ft[S::TM];
-#pragma unroll
-        for (int j = 0; j < S::TN; ++j)
-          fw[j] = *reinterpret_cast<const bf16x8*>(lb + swz(wn * S::TN * 32 + j * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int i = 0; i < S::TM; ++i)
-          ft[i] = *reinterpret_cast<const bf16x8*>(la + swz(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
+      for (int kk = 0; kk < kSteps; ++kk) {
+        if (kk + 1 < kSteps) lds_frags((kk + 1) & 1, la, lb, kk + 1);
 #pragma unroll
         for (int i = 0; i < S::TM; ++i)
 #pragma unroll
           for (int j = 0; j < S::TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], ft[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk & 1][j], ft[kk & 1][i], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) sstore(buf ^ 1);
-      __syncthreads();
+      sched_stage<kSteps, kReads, kMfma, 0>();
     }
+    // All LDS reads of this tile done before the next tile's loads refill the ring.
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
 
     // Epilogue. Lane holds token row (lane & 31) of each 32-row sub-tile and weight rows
     // 8*g + 4*(lane >> 5) + {0..3} of each 32-row weight sub-tile (g = 0..3).
@@ -202,10 +304,7 @@ __global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
     for (int i = 0; i < S::TM; ++i) {
       const int m = wm * S::TM * 32 + i * 32 + (lane & 31);
       if (m >= rows) continue;
-      const int64_t p = min(row0 + m, c.rows_bound - 1);
-      int64_t orow = SCATTER ? static_cast<int64_t>(c.scatter[p]) : p;
-      orow = min(max(orow, int64_t(0)), c.c_rows - 1);
-      uint16_t* crow = Cbase + orow * c.ldc;
+      uint16_t* crow = Cbase + min(max(out_row[i], int64_t(0)), c.c_rows - 1) * c.ldc;
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < S::TN / 2; ++j) {
@@ -218,7 +317,10 @@ __global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
             for (int r = 0; r < 4; ++r) {
               const float up = acc[i][j][4 * g + r];
               const float gate = acc[i][j + S::TN / 2][4 * g + r];
-              o[r] = f32_to_bf16_bits(up * (gate / (1.f + expf(-gate))));
+              // silu(gate) = gate / (1 + 2^(-gate * log2 e)): hardware exp2 and reciprocal,
+              // a few fp32 ulp, far below the bf16 rounding that follows
+              const float e = __builtin_amdgcn_exp2f(-gate * 1.44269504088896340736f);
+              o[r] = f32_to_bf16_bits(up * gate * __builtin_amdgcn_rcpf(1.f + e));
             }
             *reinterpret_cast<uint2*>(crow + col) =
                 make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
@@ -243,6 +345,9 @@ __global__ __launch_bounds__(S::NT) void gemm_bf16_kernel(GemmCall c) {
       }
     }
   }
+  // The last stage's clamped re-fetch may still be in flight: let every LDS write land before
+  // the workgroup's LDS is released.
+  wait_vmcnt<0>();
 }
 
 template <class S>
@@ -270,8 +375,8 @@ int gemm_bf16_tile_m(int variant) { return variant == 0 ? ShapeLarge::BM : Shape
 int gemm_bf16_pick_variant(double mean_rows_per_group) { return mean_rows_per_group >= 96.0 ? 0 : 1; }
 
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s) {
-  if (variant == 0) return launch_shape<ShapeLarge>(c, s, 1);
-  return launch_shape<ShapeSmall>(c, s, 2);
+  if (variant == 0) return launch_shape<ShapeLarge>(c, s, ShapeLarge::WG_PER_CU);
+  return launch_shape<ShapeSmall>(c, s, ShapeSmall::WG_PER_CU);
 }
 
 }  // namespace moe

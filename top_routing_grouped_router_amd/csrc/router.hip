@@ -239,8 +239,10 @@ constexpr int kXBytes = kRT * kRowB;        // 8 KiB
 constexpr int kPlaneBytes = kRE * kRowB;    // 8 KiB per bf16 plane
 constexpr int kRStage = kXBytes + 3 * kPlaneBytes;
 
+// 16-lane passes over 16 consecutive rows: slot = chunk ^ ((row >> 1) & 7) spreads them over
+// all 64 LDS banks (a 128-byte row covers half of them).
 __device__ __forceinline__ int rswz(int row, int chunk) {
-  return row * kRowB + ((chunk ^ (row & 7)) << 4);
+  return row * kRowB + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 __device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
