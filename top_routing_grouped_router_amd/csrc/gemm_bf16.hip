@@ -13,12 +13,12 @@
 //
 // Design for CDNA4:
 //   * v_mfma_f32_32x32x16_bf16. The weight rows feed the MFMA's first operand and the token
-//     rows its second, so each lane ends with 4 consecutive output columns of one token row:
-//     the epilogue writes 8-byte packed bf16 and the SwiGLU pairs up/gate in registers.
-//   * Tile = (WM*TM*32 token rows) x (WN*TN*32 weight rows) x 64 k, 4 wavefronts. The large
-//     variant is 256 x 256 (each wavefront 128 x 128: 16 MFMA accumulators of 16 floats).
-//     LDS holds two stages of both tiles (128 KiB for 256 x 256); 16-byte chunks are XOR-
-//     swizzled by row pair so fragment reads and staging writes are free of bank conflicts.
+//     rows its second, so each lane ends with 4 consecutive output columns of one token row
+//     (8 bytes of packed bf16) and the SwiGLU pairs up/gate in registers.
+//   * Tile = (WM*TM*32 token rows) x (WN*TN*32 weight rows) x 64 k, WM x WN wavefronts. The
+//     large variant is 256 x 256 with 8 wavefronts (2 x 4) of 128 token rows x 64 weight rows
+//     (8 MFMA accumulators of 16 floats each). LDS holds two stages of both tiles (128 KiB);
+//     16-byte chunks are XOR-swizzled by row pair so fragment reads are free of bank conflicts.
 //   * The A loader gathers token rows through the permutation (row = perm[p] / k), so the
 //     permuted copy of the tokens is never materialised; the GEMM2 epilogue scatters rows to
 //     assignment order, so the combine reads each token's k rows contiguously.
@@ -26,6 +26,12 @@
 //     tile sequence is cut into 8 contiguous chunks, one per XCD, and inside a chunk tiles go
 //     in groups of 4 M-tiles x all N-tiles, so the tiles an XCD runs together share A and B
 //     panels in that XCD's L2.
+//   * Operands reach LDS by DMA (global_load_lds_dwordx4, 16 bytes per lane, no register
+//     round trip); each 64-k stage is one whole 128-byte line per staged row.
+//   * Epilogue through LDS: the accumulators leave the MFMA layout as 8-byte pieces of 32
+//     different rows, so stored directly every instruction writes 32 partial lines. They are
+//     staged in the free ring slot instead and stored as whole rows (full 128-byte lines per
+//     instruction); the next tile's first stage is issued during the last staging round.
 //   * Experts with no tokens have no M-tile and their weights are never read.
 #include "common.hpp"
 
@@ -131,6 +137,7 @@ __device__ __forceinline__ void sched_stage() {
 
 template <class S, bool SWIGLU, bool GATHER, bool SCATTER>
 __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
+  static_assert(S::NSTAGE == 2, "the persistent loop runs a two-slot ring");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[S::LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   // wavefront coordinates are uniform per wavefront: keep them in scalar registers
@@ -145,87 +152,223 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   const int64_t total = total_m * ntn;
   const int xcd = blockIdx.x % kXcds;
   const int per_xcd = gridDim.x / kXcds;
-  const int slot = blockIdx.x / kXcds;
   const int64_t chunk = (total + kXcds - 1) / kXcds;
   const int nk = static_cast<int>(c.Kd / S::BK);
   const unsigned char* Ab = static_cast<const unsigned char*>(c.A);
   uint16_t* Cbase = static_cast<uint16_t*>(c.C);
 
-  // this lane's row inside a DMA load, and the logical 16-byte chunk it fetches so that the
-  // linear LDS write lands in the swizzled slot
+  // this lane's row inside a DMA load
   const int dma_row = lane / S::CHUNKS;
 
-  for (int64_t it = slot; it < chunk; it += per_xcd) {
+  // One output tile of the persistent sequence: where its rows and columns come from, the
+  // source offsets of this wavefront's DMA loads, and the output rows of this lane.
+  struct TileState {
+    int64_t row0, nt;
+    int rows;
+    const unsigned char* Bexp;
+    uint32_t src_off[S::NQ];  // byte offset of the source 16-byte chunk of load q (k-stage 0)
+  };
+  // The load index inside a stage is uniform per wavefront, so is the operand it reads.
+  auto load_is_a = [&](int q) { return wave + S::NW * q < S::BM / S::kRowsPerDma; };
+
+  auto setup = [&](int64_t it, TileState& t) {
     const int64_t lin = xcd * chunk + it;
-    if (lin >= total) break;
+    // tiles go in groups of kGroupM M-tiles x all N-tiles
     const int64_t gsz = kGroupM * ntn;
     const int64_t grp_i = lin / gsz, first_m = grp_i * kGroupM;
     const int64_t gm = min(static_cast<int64_t>(kGroupM), total_m - first_m);
     const int64_t local = lin - grp_i * gsz;
     const int64_t mt = first_m + local % gm;
-    const int64_t nt = local / gm;
-
-    int64_t row0, grp;
-    int rows;
+    t.nt = local / gm;
+    int64_t grp;
     if (c.dense_M > 0) {
-      row0 = mt * S::BM;
-      rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - row0));
+      t.row0 = mt * S::BM;
+      t.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - t.row0));
       grp = 0;
     } else {
-      row0 = c.tiles.row0[mt];
-      rows = c.tiles.rows[mt];
+      t.row0 = c.tiles.row0[mt];
+      t.rows = c.tiles.rows[mt];
       grp = c.tiles.expert[mt];
     }
-    const unsigned char* Bexp =
-        reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(c.B) + grp * c.b_group_stride);
-
-    // Per DMA load q of this wavefront: 32-bit byte offset of the source 16-byte chunk (stage 0)
-    // and whether it reads the token (A) or weight (B) operand.
-    uint32_t src_off[S::NQ];
-    bool is_a[S::NQ];
+    t.Bexp = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(c.B) + grp * c.b_group_stride);
 #pragma unroll
     for (int q = 0; q < S::NQ; ++q) {
-      const int i = wave + S::NW * q;  // load index inside the stage (uniform)
-      is_a[q] = i < S::BM / S::kRowsPerDma;
-      const int r = (is_a[q] ? i : i - S::BM / S::kRowsPerDma) * S::kRowsPerDma + dma_row;
+      const int i = wave + S::NW * q;
+      const bool is_a = load_is_a(q);
+      const int r = (is_a ? i : i - S::BM / S::kRowsPerDma) * S::kRowsPerDma + dma_row;
+      // the logical chunk this lane fetches, so that the linear LDS write lands swizzled
       const int chunk_l = (lane % S::CHUNKS) ^ ((r / S::ROWS_PER_BANKLINE) & (S::CHUNKS - 1));
-      if (is_a[q]) {
-        int64_t p = row0 + (r < rows ? r : 0);
+      if (is_a) {
+        int64_t p = t.row0 + (r < t.rows ? r : 0);
         p = min(max(p, int64_t(0)), c.rows_bound - 1);
         int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
         src = min(max(src, int64_t(0)), c.a_rows - 1);
-        src_off[q] = static_cast<uint32_t>(src * c.lda * 2 + chunk_l * 16);
+        t.src_off[q] = static_cast<uint32_t>(src * c.lda * 2 + chunk_l * 16);
       } else {
         int64_t wrow;
         if (SWIGLU) {
           const int wv = r / (S::TN * 32), qq = r % (S::TN * 32);
           const int half = qq / (S::TN * 16);
-          int64_t col = nt * (S::BN / 2) + wv * (S::TN * 16) + (qq % (S::TN * 16));
+          int64_t col = t.nt * (S::BN / 2) + wv * (S::TN * 16) + (qq % (S::TN * 16));
           col = min(col, c.N - 1);
           wrow = col + (half ? c.swiglu_h : 0);
         } else {
-          wrow = min(nt * S::BN + r, c.N - 1);
+          wrow = min(t.nt * S::BN + r, c.N - 1);
         }
-        src_off[q] = static_cast<uint32_t>(wrow * c.ldb * 2 + chunk_l * 16);
+        t.src_off[q] = static_cast<uint32_t>(wrow * c.ldb * 2 + chunk_l * 16);
       }
     }
+  };
 
-    // Issue the DMA loads of pipeline stage kt into ring slot kt % NSTAGE.
-    // Issue loads q in [q0, q1) of pipeline stage kt into ring slot `ring_slot`.
-    auto issue_part = [&](int kt, int ring_slot, int q0, int q1) {
-      unsigned char* st = lds + ring_slot * S::STAGE;
+  // DMA loads of k-stage kt of tile t into ring slot `ring_slot`.
+  auto issue = [&](const TileState& t, int kt, int ring_slot) {
+    unsigned char* st = lds + ring_slot * S::STAGE;
 #pragma unroll
-      for (int q = 0; q < S::NQ; ++q) {
-        if (q < q0 || q >= q1) continue;
-        const int i = wave + S::NW * q;
-        if (S::NI % S::NW != 0 && i >= S::NI) continue;
-        const unsigned char* g = (is_a[q] ? Ab : Bexp) + (src_off[q] + static_cast<uint32_t>(kt) * S::ROWB);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
-      }
-    };
-    auto issue = [&](int kt, int ring_slot) { issue_part(kt, ring_slot, 0, S::NQ); };
+    for (int q = 0; q < S::NQ; ++q) {
+      const int i = wave + S::NW * q;
+      if (S::NI % S::NW != 0 && i >= S::NI) continue;
+      const unsigned char* g =
+          (load_is_a(q) ? Ab : t.Bexp) + (t.src_off[q] + static_cast<uint32_t>(kt) * S::ROWB);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
+    }
+  };
 
-    f32x16 acc[S::TM][S::TN];
+  f32x16 acc[S::TM][S::TN];
+  bf16x8 fw[2][S::TN], ft[2][S::TM];
+  auto lds_frags = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
+    const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+      fw[fs][j] = *reinterpret_cast<const bf16x8*>(lb + swz<S>(wn * S::TN * 32 + j * 32 + (lane & 31), ch));
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i)
+      ft[fs][i] = *reinterpret_cast<const bf16x8*>(la + swz<S>(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
+  };
+
+  // Epilogue, staged through LDS slot 1 (slot 0 is receiving the next tile's first stage).
+  // Lane holds token row (lane & 31) of each 32-row sub-tile and weight rows
+  // 8*g + 4*(lane >> 5) + {0..3} of each 32-row weight sub-tile (g = 0..3), i.e. 8 bytes of
+  // 32 different output rows per register group: stored directly that is 32 partial lines per
+  // instruction. Instead the tile goes to LDS in bf16 and leaves as whole rows, every store
+  // instruction writing full 128-byte lines. The output tile (BM x OUTC bf16) passes in NR
+  // rounds of RR rows; round rho carries sub-tiles i in [rho*TMR, (rho+1)*TMR) of every wavefront.
+  constexpr int OUTC = SWIGLU ? S::BN / 2 : S::BN;      // output columns per tile
+  constexpr int RB = OUTC * 2;                          // bytes per output row
+  constexpr int CPR = RB / 16;                          // 16-byte chunks per output row
+  constexpr int NR = (S::BM * RB + S::STAGE - 1) / S::STAGE;
+  constexpr int TMR = S::TM / NR;
+  constexpr int RR = S::BM / NR;                        // rows per round
+  constexpr int RPI = S::NT * 16 / RB;                  // rows per store instruction
+  constexpr int KI = RR / RPI;                          // store instructions per thread per round
+  static_assert(S::TM % NR == 0 && RR % RPI == 0 && RR * RB <= S::STAGE, "epilogue staging");
+  unsigned char* stg = lds + S::STAGE;
+  // LDS byte address of byte b of staged row lr: 16-byte chunks XOR-swizzled by row, so the
+  // 32 rows of one register group land in distinct bank groups and a row read stays whole.
+  auto stg_addr = [&](int lr, int b) {
+    return lr * RB + ((((b >> 4) ^ (lr & (CPR - 1))) << 4) | (b & 15));
+  };
+  // tile row of staged row lr in round rho
+  auto tile_row = [&](int rho, int lr) {
+    const int w = lr / (TMR * 32), ii = (lr % (TMR * 32)) / 32;
+    return w * S::TM * 32 + (rho * TMR + ii) * 32 + (lr & 31);
+  };
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  // Epilogue of tile t. When `more`, stage 0 of tile nx is issued into slot 0 once slot 1 holds
+  // the last staging round: its loads then overlap the last round's reads and stores. (Issued
+  // earlier, the compiler would wait for them before the staging writes, which share LDS.)
+  auto epilogue = [&](const TileState& t, bool more, int64_t it_next, TileState& nx) {
+    const int quad = 4 * (lane >> 5);
+    const int64_t col0 = t.nt * OUTC;
+#pragma unroll
+    for (int rho = 0; rho < NR; ++rho) {
+      // Scatter indices of the rows this thread stores in this round, fetched first so their
+      // latency overlaps the LDS round trip.
+      int sidx[SCATTER ? KI : 1];
+      if constexpr (SCATTER) {
+#pragma unroll
+        for (int k = 0; k < KI; ++k) {
+          const int m = tile_row(rho, k * RPI + tid / CPR);
+          sidx[k] = c.scatter[min(t.row0 + (m < t.rows ? m : 0), c.rows_bound - 1)];
+        }
+      }
+      if (rho > 0) {  // every wavefront done reading the previous round
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+      }
+#pragma unroll
+      for (int ii = 0; ii < TMR; ++ii) {
+        const int i = rho * TMR + ii;
+        const int lr = wm * TMR * 32 + ii * 32 + (lane & 31);
+        if (SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < S::TN / 2; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint16_t o[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float up = acc[i][j][4 * g + r];
+                const float gate = acc[i][j + S::TN / 2][4 * g + r];
+                // silu(gate) = gate / (1 + 2^(-gate * log2 e)): hardware exp2 and reciprocal,
+                // a few fp32 ulp, far below the bf16 rounding that follows
+                const float e = __builtin_amdgcn_exp2f(-gate * 1.44269504088896340736f);
+                o[r] = f32_to_bf16_bits(up * gate * __builtin_amdgcn_rcpf(1.f + e));
+              }
+              const int ct = wn * (S::TN * 16) + j * 32 + 8 * g + quad;
+              *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
+                  make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                             o[2] | (static_cast<uint32_t>(o[3]) << 16));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < S::TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint16_t o[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16_bits(acc[i][j][4 * g + r]);
+              const int ct = wn * (S::TN * 32) + j * 32 + 8 * g + quad;
+              *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
+                  make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                             o[2] | (static_cast<uint32_t>(o[3]) << 16));
+            }
+          }
+        }
+      }
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      // The accumulators are dead once the last round is in LDS: set up the next tile then
+      // (its index loads, then its first DMA loads, ahead of this round's stores).
+      const int cc = tid % CPR;
+      const int64_t col = col0 + cc * 8;
+      u32x4_t v[KI];
+#pragma unroll
+      for (int k = 0; k < KI; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg_addr(k * RPI + tid / CPR, cc * 16));
+      if (rho == NR - 1 && more) {
+        setup(it_next, nx);
+        issue(nx, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < KI; ++k) {
+        const int lr = k * RPI + tid / CPR;
+        const int m = tile_row(rho, lr);
+        const int64_t orow = SCATTER ? static_cast<int64_t>(sidx[SCATTER ? k : 0]) : t.row0 + m;
+        if (m < t.rows && col < c.N)
+          *reinterpret_cast<u32x4_t*>(Cbase + min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col) = v[k];
+      }
+    }
+  };
+
+  // Persistent loop over this workgroup's tiles: it = slot, slot + per_xcd, ... inside the
+  // XCD's chunk. Stage 0 of the next tile is issued before the current tile's epilogue, so its
+  // load latency hides under the epilogue's stores.
+  int64_t it = blockIdx.x / kXcds;
+  if (it >= chunk || xcd * chunk + it >= total) return;
+  TileState cur;
+  setup(it, cur);
+  issue(cur, 0, 0);
+  for (;;) {
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
 #pragma unroll
@@ -233,48 +376,14 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    bf16x8 fw[2][S::TN], ft[2][S::TM];
-    auto lds_frags = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
-      const int ch = 2 * kk + (lane >> 5);
-#pragma unroll
-      for (int j = 0; j < S::TN; ++j)
-        fw[fs][j] = *reinterpret_cast<const bf16x8*>(lb + swz<S>(wn * S::TN * 32 + j * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int i = 0; i < S::TM; ++i)
-        ft[fs][i] = *reinterpret_cast<const bf16x8*>(la + swz<S>(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
-    };
-
-    // Output rows of this lane's token sub-tiles. The scatter indices are loaded now and only
-    // used (clamped) in the epilogue, so their latency hides under the k-loop.
-    int64_t out_row[S::TM];
-#pragma unroll
-    for (int i = 0; i < S::TM; ++i) {
-      const int m = wm * S::TM * 32 + i * 32 + (lane & 31);
-      const int64_t p = min(row0 + (m < rows ? m : 0), c.rows_bound - 1);
-      out_row[i] = SCATTER ? static_cast<int64_t>(c.scatter[p]) : p;
-    }
-
-    // Prologue: NSTAGE-1 stages in flight.
-#pragma unroll
-    for (int s0 = 0; s0 < S::NSTAGE - 1; ++s0)
-      issue(min(s0, nk - 1), s0);
-
     for (int kt = 0; kt < nk; ++kt) {
-      // Wait until this wavefront's loads of stage kt have landed (younger stages may stay in
-      // flight), then a barrier: every wavefront's part of stage kt is in LDS, and every
-      // wavefront has finished reading stage kt-1, whose ring slot is refilled below.
-      const int younger = min(S::NSTAGE - 2, nk - 1 - kt);
-      if (younger >= 2) wait_vmcnt<2 * S::NQMIN>();
-      else if (younger == 1) wait_vmcnt<S::NQMIN>();
-      else wait_vmcnt<0>();
+      // This wavefront's loads of stage kt have landed; after the barrier so have every
+      // wavefront's, and every wavefront is done reading stage kt-1, whose slot is refilled.
+      wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-
-      const unsigned char* la = lds + (kt % S::NSTAGE) * S::STAGE;
+      const unsigned char* la = lds + (kt & 1) * S::STAGE;
       const unsigned char* lb = la + S::BM * S::ROWB;
-      // Refill the ring slot freed by the barrier: stage kt+NSTAGE-1 lands while this stage
-      // computes. Past the last stage the issue is clamped to re-fetch the last stage into the
-      // idle slot (never read), which keeps the loop branch-free.
-      issue(min(kt + S::NSTAGE - 1, nk - 1), (kt + S::NSTAGE - 1) % S::NSTAGE);
+      if (kt + 1 < nk) issue(cur, kt + 1, (kt + 1) & 1);
       // k16 steps with fragments double-buffered in registers; the directives interleave step
       // kk+1's LDS reads with step kk's MFMAs so the matrix pipe does not wait on an LDS round
       // trip before every MFMA group.
@@ -293,60 +402,20 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       sched_stage<kSteps, kReads, kMfma, 0>();
     }
-    // All LDS reads of this tile done before the next tile's loads refill the ring.
+    // Every wavefront done reading this tile's last stages: slot 0 is free for the next tile.
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
 
-    // Epilogue. Lane holds token row (lane & 31) of each 32-row sub-tile and weight rows
-    // 8*g + 4*(lane >> 5) + {0..3} of each 32-row weight sub-tile (g = 0..3).
-    const int quad = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < S::TM; ++i) {
-      const int m = wm * S::TM * 32 + i * 32 + (lane & 31);
-      if (m >= rows) continue;
-      uint16_t* crow = Cbase + min(max(out_row[i], int64_t(0)), c.c_rows - 1) * c.ldc;
-      if (SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < S::TN / 2; ++j) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int64_t col = nt * (S::BN / 2) + wn * (S::TN * 16) + j * 32 + 8 * g + quad;
-            if (col >= c.N) continue;
-            uint16_t o[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float up = acc[i][j][4 * g + r];
-              const float gate = acc[i][j + S::TN / 2][4 * g + r];
-              // silu(gate) = gate / (1 + 2^(-gate * log2 e)): hardware exp2 and reciprocal,
-              // a few fp32 ulp, far below the bf16 rounding that follows
-              const float e = __builtin_amdgcn_exp2f(-gate * 1.44269504088896340736f);
-              o[r] = f32_to_bf16_bits(up * gate * __builtin_amdgcn_rcpf(1.f + e));
-            }
-            *reinterpret_cast<uint2*>(crow + col) =
-                make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                           o[2] | (static_cast<uint32_t>(o[3]) << 16));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < S::TN; ++j) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int64_t col = nt * S::BN + wn * (S::TN * 32) + j * 32 + 8 * g + quad;
-            if (col >= c.N) continue;
-            uint16_t o[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16_bits(acc[i][j][4 * g + r]);
-            *reinterpret_cast<uint2*>(crow + col) =
-                make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                           o[2] | (static_cast<uint32_t>(o[3]) << 16));
-          }
-        }
-      }
-    }
+    const int64_t it_next = it + per_xcd;
+    const bool more = it_next < chunk && xcd * chunk + it_next < total;
+    TileState nxt;
+    epilogue(cur, more, it_next, nxt);
+    if (!more) break;
+    cur = nxt;
+    it = it_next;
   }
-  // The last stage's clamped re-fetch may still be in flight: let every LDS write land before
-  // the workgroup's LDS is released.
+  // Nothing is left in flight that writes LDS (each tile's last stage issues no refill and the
+  // last tile issues no next stage), but keep the invariant explicit before LDS is released.
   wait_vmcnt<0>();
 }
 
