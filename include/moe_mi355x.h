@@ -182,7 +182,8 @@ MOE_API moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* w
  * (scores or logits, + score_bias); weights gathered / re-softmaxed, normalised and scaled.
  * Requires routing->expert_weights and routing->expert_indices; router_logits and
  * router_scores are filled when non-NULL. Uses the workspace (moe_workspace_size bytes) for
- * partial sums of the logits.
+ * partial sums of the logits and, on large layers, for the fp32 router weights split into
+ * three bf16 planes (hi + mid + lo = the fp32 value exactly) that the MFMA contraction reads.
  */
 MOE_API moe_status_t moe_router_forward(const moe_config_t* cfg, const moe_weights_t* weights,
                                 int64_t num_tokens, const void* x, moe_routing_t* routing,

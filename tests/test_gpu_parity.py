@@ -123,6 +123,10 @@ ROUTER_CASES = [
     ("latent896", 300, dict(d_model=512, latent_dim=256)),
     ("decode", None, dict(d_model=1024)),
     ("skewed", 257, dict(d_model=512, num_experts=256)),
+    # large enough for the weight-planes MFMA GEMM (>= 256 tiles of 256 tokens x 128 experts):
+    # ragged token tail and a ragged last expert tile (1020 = 7 * 128 + 124)
+    ("latent896", 8300, dict(d_model=256, num_experts=1020, latent_dim=64, hidden_size=64)),
+    ("skewed", 32768, dict(d_model=512, num_experts=256, hidden_size=64)),
 ]
 
 

@@ -145,7 +145,8 @@ struct Carve {
 };
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, z, act, yassign, total;
+  size_t logits, rscratch, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, z, act, yassign,
+      total;
   int32_t tile_cap;
 };
 
@@ -157,6 +158,7 @@ WsLayout ws_layout(const Layer& ly) {
   const int bm = expert_tile_m(ly);
   w.tile_cap = static_cast<int32_t>((A + bm - 1) / bm + E);
   w.logits = c.take(static_cast<size_t>(router_splits(ly)) * T * E * 4);  // logit partial sums
+  w.rscratch = c.take(router_scratch_bytes(ly));                            // router weight planes
   w.idx = c.take(A * 4);
   w.w = c.take(A * 4);
   w.counts = c.take(E * 4);
@@ -386,7 +388,7 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
   int32_t* inv = r.inverse_permutation ? r.inverse_permutation : at<int32_t>(ws, L.inv);
   const TileList tiles = tiles_of(ws, L);
 
-  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, s), "router logits");
+  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, at<void>(ws, L.rscratch), s), "router logits");
   MOE_TRY_HIP(launch_gate_topk(ly, parts, nsplit, false, w->score_bias, ly.router_bias ? w->router_bias : nullptr,
                                idx, wts, r.router_scores, r.router_logits, s),
               "gating/top-k");
@@ -426,11 +428,12 @@ moe_status_t moe_router_forward(const moe_config_t* c, const moe_weights_t* w, i
   const Layer ly = make_layer(c, T);
   const WsLayout L = ws_layout(ly);
   const int nsplit = router_splits(ly);
-  if (ws_bytes < L.logits + static_cast<size_t>(nsplit) * T * ly.E * 4)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the router partial sums");
+  if (ws_bytes < L.logits + static_cast<size_t>(nsplit) * T * ly.E * 4 ||
+      ws_bytes < L.rscratch + router_scratch_bytes(ly))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small for the router partial sums / weight planes");
   float* parts = at<float>(ws, L.logits);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, s), "router logits");
+  MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, at<void>(ws, L.rscratch), s), "router logits");
   MOE_TRY_HIP(launch_gate_topk(ly, parts, nsplit, false, w->score_bias, ly.router_bias ? w->router_bias : nullptr,
                                routing->expert_indices, routing->expert_weights, routing->router_scores,
                                routing->router_logits, s),

@@ -100,9 +100,15 @@ int device_cu_count();
 
 // Router logits as nsplit partial-sum planes (nsplit, T, E) f32 of x (T,d) * Wr^T; the gate
 // kernel adds the planes (fixed order) and the router bias. x is f32 or bf16 bits.
+// Router logits. Large layers (router_uses_planes) split the fp32 weights into three bf16
+// planes in `scratch` (router_scratch_bytes) and run one dense MFMA GEMM into a single logits
+// plane; otherwise a split-K kernel writes router_splits(ly) partial planes, summed in a fixed
+// order by the gate kernel.
+bool router_uses_planes(const Layer& ly);
+size_t router_scratch_bytes(const Layer& ly);
 int router_splits(const Layer& ly);
 hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, float* partials,
-                                int nsplit, hipStream_t s);
+                                int nsplit, void* scratch, hipStream_t s);
 
 // Gating + top-k + weights from logit partials (from_scores = false) or from the gating output
 // (from_scores = true: scores for softmax/sigmoid, logits for topk_softmax; nsplit ignored).
@@ -129,6 +135,7 @@ struct GemmCall {
   const void* B;            // weight rows
   int64_t ldb;
   int64_t b_group_stride;   // elements between consecutive experts' weights
+  int64_t b_plane_stride;   // elements between weight planes (planes kernel only)
   void* C;                  // output
   int64_t ldc;
   const int32_t* scatter;   // logical sorted row p -> output row scatter[p] (or NULL)
@@ -148,6 +155,10 @@ struct GemmCall {
 int gemm_bf16_tile_m(int variant);
 int gemm_bf16_pick_variant(double mean_rows_per_group);
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s);
+// Dense C(f32) = A(bf16) x sum_p B_p(bf16)^T over planes p = 0..2 (B_p at B + p*b_plane_stride):
+// the fp32-exact router contraction. N must be a multiple of 4; N-tile width below.
+hipError_t launch_gemm_bf16_planes_f32(const GemmCall& c, hipStream_t s);
+int gemm_bf16_planes_tile_n();
 
 // fp32 vector-ALU GEMM (fp32 layers and the fp32 router contraction); M-tile height 64.
 constexpr int kF32TileM = 64;

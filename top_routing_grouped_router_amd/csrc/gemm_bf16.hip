@@ -33,6 +33,8 @@
 //     staged in the free ring slot instead and stored as whole rows (full 128-byte lines per
 //     instruction); the next tile's first stage is issued during the last staging round.
 //   * Experts with no tokens have no M-tile and their weights are never read.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -44,9 +46,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 
-template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_>
+template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_, int PLANES_ = 1>
 struct Shape {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  // Weight planes summed into one product (3 for the fp32 router: its weights split exactly
+  // into three bf16 planes); each stage then stages PLANES x BN weight rows.
+  static constexpr int PLANES = PLANES_;
   static constexpr int BK = BK_;                // k per pipeline stage
   static constexpr int ROWB = BK * 2;           // bytes per staged row
   static constexpr int CHUNKS = ROWB / 16;      // 16-byte chunks per staged row
@@ -58,14 +63,14 @@ struct Shape {
   static constexpr int NT = NW * kWave;         // threads
   static constexpr int BM = WM * TM * 32;       // token rows
   static constexpr int BN = WN * TN * 32;       // weight rows
-  static constexpr int NI = (BM + BN) / kRowsPerDma;   // DMA loads per stage
+  static constexpr int BROWS = PLANES * BN;     // staged weight rows
+  static constexpr int NI = (BM + BROWS) / kRowsPerDma;  // DMA loads per stage
   static constexpr int NQ = (NI + NW - 1) / NW;        // per wavefront (upper bound)
   static constexpr int NQMIN = NI / NW;                // per wavefront (lower bound)
-  static constexpr int STAGE = (BM + BN) * ROWB;
+  static constexpr int STAGE = (BM + BROWS) * ROWB;
   static constexpr int LDS = NSTAGE * STAGE;
   static_assert(BM % kRowsPerDma == 0 && BN % kRowsPerDma == 0, "whole DMA loads per tile");
   static_assert(BK % 16 == 0 && CHUNKS >= 2 && CHUNKS <= 8, "stage depth");
-  static_assert(TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "vmcnt bookkeeping covers 2..4 stages");
   static_assert(LDS * WG_PER_CU <= 160 * 1024, "LDS budget");
 };
@@ -78,6 +83,9 @@ using ShapeLarge = Shape<2, 4, 4, 2, 64, 2, 1>;
 // 64 x 256 tile, 4 wavefronts (1 x 4) of 64 x 64: few rows per expert (decode-shaped loads);
 // 2 stages x 40 KiB, two workgroups per CU.
 using ShapeSmall = Shape<1, 4, 2, 2, 64, 2, 2>;
+// Router logits: 256 tokens x 128 experts x 3 weight planes, 8 wavefronts (2 x 4) of 128 x 32;
+// 2 stages x 80 KiB (the whole LDS).
+using ShapeRouter = Shape<2, 4, 4, 1, 64, 2, 1, 3>;
 
 // LDS is 64 banks of 4 bytes and a 16-byte access serves 16 lanes per pass. A staged row covers
 // 1/ROWS_PER_BANKLINE of the banks; chunk c of row r lives in slot c ^ ((r / ROWS_PER_BANKLINE)
@@ -135,9 +143,12 @@ __device__ __forceinline__ void sched_stage() {
   sched_stage_step<0, KSTEPS, KREADS, KMFMA, KLOADS, KLOADS>();
 }
 
-template <class S, bool SWIGLU, bool GATHER, bool SCATTER>
+template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false>
 __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
   static_assert(S::NSTAGE == 2, "the persistent loop runs a two-slot ring");
+  static_assert(!SWIGLU || S::TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
+  static_assert(!SWIGLU || S::PLANES == 1, "planes are for plain products");
+  using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[S::LDS];
   const int tid = threadIdx.x, lane = tid & 63;
   // wavefront coordinates are uniform per wavefront: keep them in scalar registers
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   const int64_t chunk = (total + kXcds - 1) / kXcds;
   const int nk = static_cast<int>(c.Kd / S::BK);
   const unsigned char* Ab = static_cast<const unsigned char*>(c.A);
-  uint16_t* Cbase = static_cast<uint16_t*>(c.C);
+  OutT* Cbase = static_cast<OutT*>(c.C);
 
   // this lane's row inside a DMA load
   const int dma_row = lane / S::CHUNKS;
@@ -206,16 +217,19 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         t.src_off[q] = static_cast<uint32_t>(src * c.lda * 2 + chunk_l * 16);
       } else {
         int64_t wrow;
+        // weight rows of plane p follow those of plane p-1
+        const int plane = S::PLANES == 1 ? 0 : r / S::BN, rp = S::PLANES == 1 ? r : r % S::BN;
         if (SWIGLU) {
-          const int wv = r / (S::TN * 32), qq = r % (S::TN * 32);
+          const int wv = rp / (S::TN * 32), qq = rp % (S::TN * 32);
           const int half = qq / (S::TN * 16);
           int64_t col = t.nt * (S::BN / 2) + wv * (S::TN * 16) + (qq % (S::TN * 16));
           col = min(col, c.N - 1);
           wrow = col + (half ? c.swiglu_h : 0);
         } else {
-          wrow = min(t.nt * S::BN + r, c.N - 1);
+          wrow = min(t.nt * S::BN + rp, c.N - 1);
         }
-        t.src_off[q] = static_cast<uint32_t>(wrow * c.ldb * 2 + chunk_l * 16);
+        const int64_t pbase = S::PLANES == 1 ? 0 : plane * c.b_plane_stride;
+        t.src_off[q] = static_cast<uint32_t>((pbase + wrow * c.ldb) * 2 + chunk_l * 16);
       }
     }
   };
@@ -234,12 +248,15 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   };
 
   f32x16 acc[S::TM][S::TN];
-  bf16x8 fw[2][S::TN], ft[2][S::TM];
+  bf16x8 fw[2][S::PLANES][S::TN], ft[2][S::TM];
   auto lds_frags = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
     const int ch = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < S::TN; ++j)
-      fw[fs][j] = *reinterpret_cast<const bf16x8*>(lb + swz<S>(wn * S::TN * 32 + j * 32 + (lane & 31), ch));
+    for (int pl = 0; pl < S::PLANES; ++pl)
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j)
+        fw[fs][pl][j] = *reinterpret_cast<const bf16x8*>(
+            lb + swz<S>(pl * S::BN + wn * S::TN * 32 + j * 32 + (lane & 31), ch));
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
       ft[fs][i] = *reinterpret_cast<const bf16x8*>(la + swz<S>(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
@@ -253,7 +270,9 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // instruction writing full 128-byte lines. The output tile (BM x OUTC bf16) passes in NR
   // rounds of RR rows; round rho carries sub-tiles i in [rho*TMR, (rho+1)*TMR) of every wavefront.
   constexpr int OUTC = SWIGLU ? S::BN / 2 : S::BN;      // output columns per tile
-  constexpr int RB = OUTC * 2;                          // bytes per output row
+  constexpr int EB = static_cast<int>(sizeof(OutT));    // bytes per output element
+  constexpr int EPC = 16 / EB;                          // output elements per 16-byte chunk
+  constexpr int RB = OUTC * EB;                         // bytes per output row
   constexpr int CPR = RB / 16;                          // 16-byte chunks per output row
   constexpr int NR = (S::BM * RB + S::STAGE - 1) / S::STAGE;
   constexpr int TMR = S::TM / NR;
@@ -325,13 +344,18 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           for (int j = 0; j < S::TN; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              uint16_t o[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16_bits(acc[i][j][4 * g + r]);
               const int ct = wn * (S::TN * 32) + j * 32 + 8 * g + quad;
-              *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
-                  make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                             o[2] | (static_cast<uint32_t>(o[3]) << 16));
+              if constexpr (OUT_F32) {
+                *reinterpret_cast<float4*>(stg + stg_addr(lr, ct * 4)) =
+                    make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+              } else {
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16_bits(acc[i][j][4 * g + r]);
+                *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
+                    make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                               o[2] | (static_cast<uint32_t>(o[3]) << 16));
+              }
             }
           }
         }
@@ -341,7 +365,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // The accumulators are dead once the last round is in LDS: set up the next tile then
       // (its index loads, then its first DMA loads, ahead of this round's stores).
       const int cc = tid % CPR;
-      const int64_t col = col0 + cc * 8;
+      const int64_t col = col0 + cc * EPC;
       u32x4_t v[KI];
 #pragma unroll
       for (int k = 0; k < KI; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg_addr(k * RPI + tid / CPR, cc * 16));
@@ -388,8 +412,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // kk+1's LDS reads with step kk's MFMAs so the matrix pipe does not wait on an LDS round
       // trip before every MFMA group.
       constexpr int kSteps = S::BK / 16;
-      constexpr int kReads = S::TM + S::TN;   // LDS fragment reads per k16 step
-      constexpr int kMfma = S::TM * S::TN;    // MFMAs per k16 step
+      constexpr int kReads = S::TM + S::PLANES * S::TN;  // LDS fragment reads per k16 step
+      constexpr int kMfma = S::TM * S::TN * S::PLANES;   // MFMAs per k16 step
       lds_frags(0, la, lb, 0);
 #pragma unroll
       for (int kk = 0; kk < kSteps; ++kk) {
@@ -398,7 +422,9 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         for (int i = 0; i < S::TM; ++i)
 #pragma unroll
           for (int j = 0; j < S::TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk & 1][j], ft[kk & 1][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int pl = S::PLANES - 1; pl >= 0; --pl)  // smallest plane first
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk & 1][pl][j], ft[kk & 1][i], acc[i][j], 0, 0, 0);
       }
       sched_stage<kSteps, kReads, kMfma, 0>();
     }
@@ -417,6 +443,17 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // Nothing is left in flight that writes LDS (each tile's last stage issues no refill and the
   // last tile issues no next stage), but keep the invariant explicit before LDS is released.
   wait_vmcnt<0>();
+}
+
+template <class S>
+int64_t persistent_grid(const GemmCall& c, int wg_per_cu) {
+  const int64_t cols_per_tile = c.swiglu_h > 0 ? S::BN / 2 : S::BN;
+  const int64_t ntn = (c.N + cols_per_tile - 1) / cols_per_tile;
+  const int64_t tiles_upper = c.dense_M > 0 ? ((c.dense_M + S::BM - 1) / S::BM) * ntn
+                                            : static_cast<int64_t>(c.tiles.cap) * ntn;
+  if (tiles_upper <= 0 || c.rows_bound <= 0) return 0;
+  const int64_t grid = std::min<int64_t>(tiles_upper, static_cast<int64_t>(device_cu_count()) * wg_per_cu);
+  return ((grid + kXcds - 1) / kXcds) * kXcds;  // whole XCD rounds
 }
 
 template <class S>
@@ -440,6 +477,18 @@ hipError_t launch_shape(const GemmCall& c, hipStream_t s, int wg_per_cu) {
 }  // namespace
 
 int gemm_bf16_tile_m(int variant) { return variant == 0 ? ShapeLarge::BM : ShapeSmall::BM; }
+
+int gemm_bf16_planes_tile_n() { return ShapeRouter::BN; }
+
+hipError_t launch_gemm_bf16_planes_f32(const GemmCall& c, hipStream_t s) {
+  // dense fp32 output only: no gather, scatter, SwiGLU or expert groups
+  if (c.dense_M <= 0 || c.gather || c.scatter || c.swiglu_h > 0 || c.N % 4 != 0) return hipErrorInvalidValue;
+  const int64_t grid = persistent_grid<ShapeRouter>(c, ShapeRouter::WG_PER_CU);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<ShapeRouter, false, false, false, true>), dim3(static_cast<unsigned>(grid)),
+                     dim3(ShapeRouter::NT), 0, s, c);
+  return hipGetLastError();
+}
 
 int gemm_bf16_pick_variant(double mean_rows_per_group) { return mean_rows_per_group >= 96.0 ? 0 : 1; }
 

@@ -30,6 +30,8 @@
 // once, coalesced; the kernel is bound by HBM/L2 reads of the logits.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -249,6 +251,34 @@ __device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
   return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
 
+// w = hi + mid + lo exactly, each a bf16 (8 significant bits): hi = bf16(w), and each next
+// plane rounds what the previous ones left (the differences are exact in fp32). The products
+// x * plane are then exact in the MFMA's fp32 accumulation, which sums them in fp32.
+__device__ __forceinline__ void split3_bf16(float w, uint16_t& hi, uint16_t& mi, uint16_t& lo) {
+  hi = f32_to_bf16_bits(w);
+  const float r1 = w - bf16_bits_to_f32(hi);
+  mi = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(mi);
+  lo = f32_to_bf16_bits(r2);
+}
+
+// The router weights (E, d) fp32 as three bf16 planes (3, E, d): hi, mid, lo. Four elements per
+// thread, grid-stride.
+__global__ __launch_bounds__(256) void split_planes_kernel(const float4* __restrict__ w, uint2* __restrict__ planes,
+                                                           int64_t n4) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float4 v = w[i];
+    uint16_t h[4], m[4], l[4];
+    split3_bf16(v.x, h[0], m[0], l[0]);
+    split3_bf16(v.y, h[1], m[1], l[1]);
+    split3_bf16(v.z, h[2], m[2], l[2]);
+    split3_bf16(v.w, h[3], m[3], l[3]);
+    planes[i] = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+    planes[n4 + i] = make_uint2(pack2(m[0], m[1]), pack2(m[2], m[3]));
+    planes[2 * n4 + i] = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+  }
+}
+
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ Wr,
                                                           float* __restrict__ part, int64_t T, int E,
@@ -301,14 +331,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
       const int c = tid + 256 * q, row = c >> 4, c4 = c & 15;
       uint16_t hi[4], mi[4], lo[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float w = rw[q][r];
-        hi[r] = f32_to_bf16_bits(w);
-        const float r1 = w - bf16_bits_to_f32(hi[r]);
-        mi[r] = f32_to_bf16_bits(r1);
-        const float r2 = r1 - bf16_bits_to_f32(mi[r]);
-        lo[r] = f32_to_bf16_bits(r2);
-      }
+      for (int r = 0; r < 4; ++r) split3_bf16(rw[q][r], hi[r], mi[r], lo[r]);
       const int off = rswz(row, c4 >> 1) + (c4 & 1) * 8;
       unsigned char* pl = base + kXBytes;
       *reinterpret_cast<uint2*>(pl + off) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
@@ -377,8 +400,20 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 
 }  // namespace
 
+bool router_uses_planes(const Layer& ly) {
+  // The planes path runs the router as one large dense MFMA GEMM (tiles of 256 tokens x
+  // gemm_bf16_planes_tile_n() experts): worth it once those tiles cover the chip.
+  if (!ly.bf16 || ly.E % 4 != 0 || ly.E < 128) return false;
+  const int64_t tn = gemm_bf16_planes_tile_n();
+  return ((ly.T + 255) / 256) * ((ly.E + tn - 1) / tn) >= 256;
+}
+
+size_t router_scratch_bytes(const Layer& ly) {
+  return router_uses_planes(ly) ? static_cast<size_t>(3) * ly.E * ly.d * 2 : 0;
+}
+
 int router_splits(const Layer& ly) {
-  if (!ly.bf16) return 1;
+  if (!ly.bf16 || router_uses_planes(ly)) return 1;
   const int64_t tiles = ((ly.T + kRT - 1) / kRT) * ((ly.E + kRE - 1) / kRE);
   const int nk = static_cast<int>(ly.d / kRBK);
   int s = 1;
@@ -418,8 +453,31 @@ hipError_t launch_gate_topk(const Layer& ly, const float* input, int nsplit, boo
 }
 
 hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr, float* partials,
-                                int nsplit, hipStream_t s) {
+                                int nsplit, void* scratch, hipStream_t s) {
   if (ly.T <= 0) return hipSuccess;
+  if (router_uses_planes(ly)) {
+    const int64_t n4 = static_cast<int64_t>(ly.E) * ly.d / 4;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n4 + 255) / 256, 4096));
+    hipLaunchKernelGGL(split_planes_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float4*>(Wr),
+                       static_cast<uint2*>(scratch), n4);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemmCall c{};
+    c.A = x;
+    c.lda = ly.d;
+    c.B = scratch;
+    c.ldb = ly.d;
+    c.b_plane_stride = static_cast<int64_t>(ly.E) * ly.d;
+    c.C = partials;
+    c.ldc = ly.E;
+    c.N = ly.E;
+    c.Kd = ly.d;
+    c.dense_M = ly.T;
+    c.a_rows = ly.T;
+    c.c_rows = ly.T;
+    c.rows_bound = ly.T;
+    return launch_gemm_bf16_planes_f32(c, s);
+  }
   if (ly.bf16) {
     const dim3 g(static_cast<unsigned>((ly.T + kRT - 1) / kRT), static_cast<unsigned>((ly.E + kRE - 1) / kRE),
                  static_cast<unsigned>(nsplit));
