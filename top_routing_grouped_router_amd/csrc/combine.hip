@@ -11,6 +11,8 @@
 //     and cast to the up-projection weight's dtype.
 // One block per token, 16-byte loads and stores, fp32 math. HBM-bound: it reads k*K and
 // writes K elements per token.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -53,30 +55,48 @@ struct Vec16<float> {
   }
 };
 
-template <typename T, bool NORM>
+// One block per token, sized to the row: NT threads (64..256) each own CH 16-byte chunks of
+// the K-element row. The k assignment rows are loaded several at a time (8 / CH) before any of
+// them is used, so their loads overlap; accumulation stays in j order.
+template <typename T, bool NORM, int CH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__ y, const float* __restrict__ w,
                                                            const float* __restrict__ g, T* __restrict__ out,
                                                            int k, int K, float eps) {
   constexpr int V = Vec16<T>::N;
+  constexpr int kBatch = CH >= 8 ? 1 : 8 / CH;  // rows in flight: 8 x 16 bytes per thread
+  const int nt = blockDim.x;
   const int64_t t = blockIdx.x;
   const int nch = K / V;
-  float o[kMaxChunks][V];
+  float o[CH][V];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c)
+  for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int q = 0; q < V; ++q) o[c][q] = 0.f;
 
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
-    const T* yr = y + (t * k + j) * static_cast<int64_t>(K);
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    uint4 raw[kBatch][CH];
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int ci = threadIdx.x + c * kThreads;
-      if (ci < nch) {
-        float v[V];
-        Vec16<T>::load(yr + ci * V, v);
+    for (int u = 0; u < kBatch; ++u) {
+      const T* yr = y + (t * k + j0 + u) * static_cast<int64_t>(K);
 #pragma unroll
-        for (int q = 0; q < V; ++q) o[c][q] = fmaf(wj, v[q], o[c][q]);
+      for (int c = 0; c < CH; ++c) {
+        const int ci = threadIdx.x + c * nt;
+        if (j0 + u < k && ci < nch) raw[u][c] = *reinterpret_cast<const uint4*>(yr + ci * V);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (j0 + u >= k) break;
+      const float wj = w[t * k + j0 + u];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int ci = threadIdx.x + c * nt;
+        if (ci < nch) {
+          float v[V];
+          Vec16<T>::load(reinterpret_cast<const T*>(&raw[u][c]), v);
+#pragma unroll
+          for (int q = 0; q < V; ++q) o[c][q] = fmaf(wj, v[q], o[c][q]);
+        }
       }
     }
   }
@@ -86,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
     __shared__ float red[kThreads / kWave];
     float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int ci = threadIdx.x + c * kThreads;
+    for (int c = 0; c < CH; ++c) {
+      const int ci = threadIdx.x + c * nt;
       if (ci < nch) {
 #pragma unroll
         for (int q = 0; q < V; ++q) ss = fmaf(o[c][q], o[c][q], ss);
@@ -97,15 +117,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
-#pragma unroll
-    for (int i = 0; i < kThreads / kWave; ++i) tot += red[i];
+    for (int i = 0; i < nt / kWave; ++i) tot += red[i];
     scale = 1.f / sqrtf(tot / static_cast<float>(K) + eps);
   }
 
   T* orow = out + t * static_cast<int64_t>(K);
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const int ci = threadIdx.x + c * kThreads;
+  for (int c = 0; c < CH; ++c) {
+    const int ci = threadIdx.x + c * nt;
     if (ci < nch) {
       float v[V];
 #pragma unroll
@@ -122,17 +141,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
   }
 }
 
+template <typename T, bool NORM>
+void launch_tn(const Layer& ly, const void* y, const float* w, const float* g, void* out, hipStream_t s) {
+  const int K = static_cast<int>(ly.K);
+  const int nch = K / Vec16<T>::N;
+  const int nt = std::min(kThreads, ((nch + kWave - 1) / kWave) * kWave);
+  const int ch = (nch + nt - 1) / nt;
+  const dim3 grid(static_cast<unsigned>(ly.T)), block(static_cast<unsigned>(nt));
+  const T* yy = static_cast<const T*>(y);
+  T* oo = static_cast<T*>(out);
+  if (ch <= 1) hipLaunchKernelGGL((combine_kernel<T, NORM, 1>), grid, block, 0, s, yy, w, g, oo, ly.k, K, ly.norm_eps);
+  else if (ch <= 2) hipLaunchKernelGGL((combine_kernel<T, NORM, 2>), grid, block, 0, s, yy, w, g, oo, ly.k, K, ly.norm_eps);
+  else if (ch <= 4) hipLaunchKernelGGL((combine_kernel<T, NORM, 4>), grid, block, 0, s, yy, w, g, oo, ly.k, K, ly.norm_eps);
+  else hipLaunchKernelGGL((combine_kernel<T, NORM, kMaxChunks>), grid, block, 0, s, yy, w, g, oo, ly.k, K, ly.norm_eps);
+}
+
 template <typename T>
 void launch_t(const Layer& ly, const void* y, const float* w, const float* g, bool norm, void* out,
               hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ly.T)), block(kThreads);
-  const int K = static_cast<int>(ly.K);
-  if (norm)
-    hipLaunchKernelGGL((combine_kernel<T, true>), grid, block, 0, s, static_cast<const T*>(y), w, g,
-                       static_cast<T*>(out), ly.k, K, ly.norm_eps);
-  else
-    hipLaunchKernelGGL((combine_kernel<T, false>), grid, block, 0, s, static_cast<const T*>(y), w, g,
-                       static_cast<T*>(out), ly.k, K, ly.norm_eps);
+  if (norm) launch_tn<T, true>(ly, y, w, g, out, s);
+  else launch_tn<T, false>(ly, y, w, g, out, s);
 }
 
 }  // namespace

@@ -84,8 +84,16 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = i * kWave + lane;
     if (e < E) {
+      // Partial planes summed in plane order; loaded eight at a time so the loads overlap.
       float acc = row[e];
-      for (int p = 1; p < a.nsplit; ++p) acc += row[p * plane + e];
+      for (int p0 = 1; p0 < a.nsplit; p0 += 8) {
+        float pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pv[u] = (p0 + u < a.nsplit) ? row[(p0 + u) * plane + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (p0 + u < a.nsplit) acc += pv[u];
+      }
       if (!FROM_SCORES && a.router_bias) acc += a.router_bias[e];
       v[i] = acc;
       if (!FROM_SCORES && a.logits_out) a.logits_out[t * E + e] = acc;
