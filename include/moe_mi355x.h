@@ -46,7 +46,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
 
@@ -220,9 +220,14 @@ MOE_API moe_status_t moe_permute(const moe_config_t* cfg, int64_t num_tokens,
 /*
  * Latent down-projection ([OC3 "Латентная проекция экспертов"], prepare_routed_input):
  * z (T, L) D = x (T, d_model) D * down_proj^T, fp32 accumulation. UNSUPPORTED without latent.
+ * ws is optional (NULL: none): with few tokens the projection splits its contraction over the
+ * chip and keeps fp32 partial sums there; without it the contraction runs unsplit (same
+ * result, slower). A non-NULL ws must hold moe_workspace_size(cfg, num_tokens) bytes
+ * (WORKSPACE_TOO_SMALL otherwise).
  */
 MOE_API moe_status_t moe_latent_down(const moe_config_t* cfg, const moe_weights_t* weights,
-                             int64_t num_tokens, const void* x, void* z, void* stream);
+                             int64_t num_tokens, const void* x, void* z, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * Routed experts ([OC3 "Вычисления экспертов и точность"], [OC3 "SwiGLU с квантизацией"]):
@@ -252,9 +257,11 @@ MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const moe_weights_t* w
 /*
  * Latent up-projection ([OC3 "Латентная проекция экспертов"], restore_routed_output): y
  * (T, d_model) D = n (T, L) D * up_proj^T, fp32 accumulation. UNSUPPORTED without latent.
+ * ws as for moe_latent_down.
  */
 MOE_API moe_status_t moe_latent_up(const moe_config_t* cfg, const moe_weights_t* weights,
-                           int64_t num_tokens, const void* n, void* y, void* stream);
+                           int64_t num_tokens, const void* n, void* y, void* ws, size_t ws_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

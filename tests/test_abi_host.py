@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_size():
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     c = moe._CConfig()
     assert moe._config_default(ctypes.byref(c)) == 0
     assert c.struct_size == ctypes.sizeof(moe._CConfig)
@@ -133,5 +133,13 @@ def test_forward_argument_errors_before_any_gpu_call():
     assert b"down_proj" in moe._last_error()
     # stage calls
     assert moe._route_from_scores(ctypes.byref(c), T, fake, None, None, fake, None) == 1
-    assert moe._latent_down(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None) == 2
+    assert moe._latent_down(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None, 0, None) == 2
+    assert moe._latent_up(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None, 0, None) == 2
+    # a workspace that is given must be whole
+    assert moe._latent_down(ctypes.byref(lat), ctypes.byref(w), T, fake, fake, fake, 16, None) == 1
+    wl = moe._CWeights()
+    wl.down_proj = wl.up_proj = fake
+    need_l = moe.workspace_size(workloads.layer_config("latent896"), T)
+    assert moe._latent_down(ctypes.byref(lat), ctypes.byref(wl), T, fake, fake, fake, need_l - 1, None) == 3
+    assert moe._latent_up(ctypes.byref(lat), ctypes.byref(wl), T, fake, fake, fake, need_l - 1, None) == 3
     assert moe._permute(ctypes.byref(c), T, fake, fake, fake, fake, fake, fake, 16, None) == 3

@@ -12,6 +12,8 @@ the oracle from them) and compare element by element:
   * moe_forward: whole-layer parity at reduced shapes (every token) that span several tiles
     with ragged tails.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -251,6 +253,34 @@ def test_latent_projections(T):
     torch.cuda.synchronize()
     assert_close(np32(z), O.prepare_routed_input(cfgO, np32(x), np32(w["down_proj"])), "bf16", "down")
     assert_close(np32(y), np32(n).astype(np.float64) @ np32(w["up_proj"]).astype(np.float64).T, "bf16", "up")
+
+
+@pytest.mark.parametrize("T", [1, 17, 64])
+def test_latent_projections_few_tokens(T):
+    """Decode-shaped projections (d_model 4096, latent 1024): the skinny weight-streaming GEMM,
+    split over the chip with a workspace and unsplit without one."""
+    banner(f"skinny latent projections T={T}")
+    cfg, w, x = workloads.make_workload("decode", tokens=T, num_experts=8)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    wg = to_device_weights(w)
+    L, d = cfg["latent_dim"], cfg["d_model"]
+    n = torch.randn((T, L), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    ref_z = O.prepare_routed_input(cfgO, np32(x), np32(w["down_proj"]))
+    ref_y = np32(n).astype(np.float64) @ np32(w["up_proj"]).astype(np.float64).T
+    c, cw = moe.MoEConfig.of(cfg).to_c(), moe._c_weights(moe.MoEConfig.of(cfg), wg)
+    xg, ng = x.cuda(), n.cuda()
+    for with_ws in (True, False):
+        z = torch.empty((T, L), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(moe.workspace_size(cfg, T), dtype=torch.uint8, device="cuda") if with_ws else None
+        args = (moe._ptr(ws), ws.numel()) if with_ws else (None, 0)
+        moe._check(moe._latent_down(ctypes.byref(c), ctypes.byref(cw), T, moe._ptr(xg), moe._ptr(z), *args,
+                                    moe._stream()))
+        moe._check(moe._latent_up(ctypes.byref(c), ctypes.byref(cw), T, moe._ptr(ng), moe._ptr(y), *args,
+                                  moe._stream()))
+        torch.cuda.synchronize()
+        assert_close(np32(z), ref_z, "bf16", f"down (workspace {with_ws})")
+        assert_close(np32(y), ref_y, "bf16", f"up (workspace {with_ws})")
 
 
 # --------------------------------------------------------------------------- whole layer

@@ -82,11 +82,13 @@ _route_from_scores = _sig("moe_route_from_scores", c_i32, _P(_CConfig), c_i64, c
                           c_vp, c_vp)
 _permute = _sig("moe_permute", c_i32, _P(_CConfig), c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                 ctypes.c_size_t, c_vp)
-_latent_down = _sig("moe_latent_down", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp)
+_latent_down = _sig("moe_latent_down", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp,
+                    ctypes.c_size_t, c_vp)
 _experts_forward = _sig("moe_experts_forward", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp,
                         c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp)
 _combine = _sig("moe_combine", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp, c_vp)
-_latent_up = _sig("moe_latent_up", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp)
+_latent_up = _sig("moe_latent_up", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp,
+                  ctypes.c_size_t, c_vp)
 
 
 class MoEError(RuntimeError):
@@ -337,7 +339,9 @@ def latent_down(cfg, weights: dict, x: torch.Tensor) -> torch.Tensor:
     _expect(x, (T, cfg.d_model), cfg.torch_dtype, "x")
     z = torch.empty((T, cfg.latent_dim or 0), dtype=cfg.torch_dtype, device=x.device)
     c, cw = cfg.to_c(), _c_weights(cfg, weights)
-    _check(_latent_down(ctypes.byref(c), ctypes.byref(cw), T, _ptr(x), _ptr(z), _stream()))
+    ws = torch.empty(max(workspace_size(cfg, T), 1), dtype=torch.uint8, device=x.device)
+    _check(_latent_down(ctypes.byref(c), ctypes.byref(cw), T, _ptr(x), _ptr(z), _ptr(ws), ws.numel(),
+                        _stream()))
     return z
 
 
@@ -376,5 +380,7 @@ def latent_up(cfg, weights: dict, n: torch.Tensor) -> torch.Tensor:
     _expect(n, (T, cfg.latent_dim or 0), cfg.torch_dtype, "n")
     y = torch.empty((T, cfg.d_model), dtype=cfg.torch_dtype, device=n.device)
     c, cw = cfg.to_c(), _c_weights(cfg, weights)
-    _check(_latent_up(ctypes.byref(c), ctypes.byref(cw), T, _ptr(n), _ptr(y), _stream()))
+    ws = torch.empty(max(workspace_size(cfg, T), 1), dtype=torch.uint8, device=n.device)
+    _check(_latent_up(ctypes.byref(c), ctypes.byref(cw), T, _ptr(n), _ptr(y), _ptr(ws), ws.numel(),
+                      _stream()))
     return y

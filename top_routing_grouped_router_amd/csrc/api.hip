@@ -9,6 +9,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -134,6 +135,8 @@ int expert_variant(const Layer& ly) {
 }
 int expert_tile_m(const Layer& ly) { return ly.bf16 ? gemm_bf16_tile_m(expert_variant(ly)) : kF32TileM; }
 int dense_variant(int64_t rows) { return gemm_bf16_pick_variant(static_cast<double>(rows)); }
+// Latent projections of few tokens run on the skinny weight-streaming GEMM.
+bool uses_skinny(const Layer& ly) { return ly.bf16 && ly.L > 0 && ly.T <= kSkinnyMaxRows; }
 
 struct Carve {
   size_t off = 0;
@@ -146,7 +149,7 @@ struct Carve {
 
 struct WsLayout {
   size_t logits, rscratch, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, z, act, yassign,
-      total;
+      skinny, skinny_bytes, total;
   int32_t tile_cap;
 };
 
@@ -173,6 +176,11 @@ WsLayout ws_layout(const Layer& ly) {
   w.z = c.take(ly.L ? T * static_cast<size_t>(ly.L) * es : 0);
   w.act = c.take(A * static_cast<size_t>(ly.h) * es);
   w.yassign = c.take(A * static_cast<size_t>(ly.K) * es);
+  // split-K partials of the skinny latent projections (few tokens)
+  w.skinny_bytes = uses_skinny(ly) ? std::max(gemm_skinny_partial_bytes(ly.T, ly.L, ly.d),
+                                              gemm_skinny_partial_bytes(ly.T, ly.d, ly.L))
+                                   : 0;
+  w.skinny = c.take(w.skinny_bytes);
   w.total = c.off;
   return w;
 }
@@ -219,7 +227,7 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool r
 // ------------------------------------------------------------------ launch helpers
 
 hipError_t run_dense(const Layer& ly, int64_t rows, const void* A, int64_t lda, const void* B, int64_t N,
-                     int64_t Kd, void* C, hipStream_t s) {
+                     int64_t Kd, void* C, float* partials, size_t partial_bytes, hipStream_t s) {
   GemmCall c{};
   c.A = A;
   c.lda = lda;
@@ -233,6 +241,7 @@ hipError_t run_dense(const Layer& ly, int64_t rows, const void* A, int64_t lda, 
   c.a_rows = rows;
   c.c_rows = rows;
   c.rows_bound = rows;
+  if (ly.bf16 && rows <= kSkinnyMaxRows && N % 64 == 0) return launch_gemm_skinny(c, partials, partial_bytes, s);
   if (ly.bf16) return launch_gemm_bf16(c, dense_variant(rows), s);
   return launch_gemm_f32(c, false, nullptr, s);
 }
@@ -397,7 +406,9 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
               "dispatch");
   const void* z = x;
   if (ly.L) {
-    MOE_TRY_HIP(run_dense(ly, T, x, ly.d, w->down_proj, ly.L, ly.d, at<void>(ws, L.z), s), "latent down");
+    MOE_TRY_HIP(run_dense(ly, T, x, ly.d, w->down_proj, ly.L, ly.d, at<void>(ws, L.z), at<float>(ws, L.skinny),
+                          L.skinny_bytes, s),
+                "latent down");
     z = at<void>(ws, L.z);
   }
   MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), at<void>(ws, L.yassign), s),
@@ -406,7 +417,8 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
     void* n = at<void>(ws, L.z);  // z is dead after the first expert GEMM
     MOE_TRY_HIP(launch_combine(ly, at<void>(ws, L.yassign), wts, w->up_proj_input_norm_weight, ly.up_norm, n, s),
                 "combine");
-    MOE_TRY_HIP(run_dense(ly, T, n, ly.L, w->up_proj, ly.d, ly.L, y, s), "latent up");
+    MOE_TRY_HIP(run_dense(ly, T, n, ly.L, w->up_proj, ly.d, ly.L, y, at<float>(ws, L.skinny), L.skinny_bytes, s),
+                "latent up");
   } else {
     MOE_TRY_HIP(launch_combine(ly, at<void>(ws, L.yassign), wts, nullptr, false, y, s), "combine");
   }
@@ -485,7 +497,7 @@ moe_status_t moe_permute(const moe_config_t* c, int64_t T, const int32_t* idx, i
 }
 
 moe_status_t moe_latent_down(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* z,
-                             void* stream) {
+                             void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = validate_config(c);
   if (st != MOE_OK) return st;
   if (!c->latent_dim) return fail(MOE_ERR_UNSUPPORTED, "latent_down needs latent_dim > 0");
@@ -496,7 +508,11 @@ moe_status_t moe_latent_down(const moe_config_t* c, const moe_weights_t* w, int6
   if ((st = need(x, "x")) != MOE_OK) return st;
   if ((st = need(z, "z")) != MOE_OK) return st;
   const Layer ly = make_layer(c, T);
-  MOE_TRY_HIP(run_dense(ly, T, x, ly.d, w->down_proj, ly.L, ly.d, z, static_cast<hipStream_t>(stream)),
+  const WsLayout L = ws_layout(ly);
+  if (ws && ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  float* parts = ws ? at<float>(ws, L.skinny) : nullptr;
+  MOE_TRY_HIP(run_dense(ly, T, x, ly.d, w->down_proj, ly.L, ly.d, z, parts, ws ? L.skinny_bytes : 0,
+                        static_cast<hipStream_t>(stream)),
               "latent down");
   return ok();
 }
@@ -542,7 +558,7 @@ moe_status_t moe_combine(const moe_config_t* c, const moe_weights_t* w, int64_t 
 }
 
 moe_status_t moe_latent_up(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* n, void* y,
-                           void* stream) {
+                           void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = validate_config(c);
   if (st != MOE_OK) return st;
   if (!c->latent_dim) return fail(MOE_ERR_UNSUPPORTED, "latent_up needs latent_dim > 0");
@@ -553,7 +569,11 @@ moe_status_t moe_latent_up(const moe_config_t* c, const moe_weights_t* w, int64_
   if ((st = need(n, "n")) != MOE_OK) return st;
   if ((st = need(y, "y")) != MOE_OK) return st;
   const Layer ly = make_layer(c, T);
-  MOE_TRY_HIP(run_dense(ly, T, n, ly.L, w->up_proj, ly.d, ly.L, y, static_cast<hipStream_t>(stream)),
+  const WsLayout L = ws_layout(ly);
+  if (ws && ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  float* parts = ws ? at<float>(ws, L.skinny) : nullptr;
+  MOE_TRY_HIP(run_dense(ly, T, n, ly.L, w->up_proj, ly.d, ly.L, y, parts, ws ? L.skinny_bytes : 0,
+                        static_cast<hipStream_t>(stream)),
               "latent up");
   return ok();
 }

@@ -49,6 +49,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave-uniform reductions through DPP: four lane-exchange steps reduce each 16-lane row
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror: afterwards every lane
+// of a row holds the row's result), then the four row results are read into scalar registers
+// and combined in a fixed order ((r0 op r1) op (r2 op r3)). No LDS round trips; the result is
+// the same on every lane and, for sums, the order is fixed, so it is deterministic. Every lane
+// of the wavefront must be active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<0xB1>(v));
+  v = op(v, dpp_u32<0x4E>(v));
+  v = op(v, dpp_u32<0x141>(v));
+  v = op(v, dpp_u32<0x140>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ int32_t wave_min_i32_dpp(int32_t v) {
+  return static_cast<int32_t>(wave_reduce_u32(static_cast<uint32_t>(v), [](uint32_t a, uint32_t b) {
+    return static_cast<int32_t>(a) < static_cast<int32_t>(b) ? a : b;
+  }));
+}
+__device__ __forceinline__ float wave_max_f32_dpp(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_f32_dpp(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -159,6 +200,14 @@ hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s);
 // the fp32-exact router contraction. N must be a multiple of 4; N-tile width below.
 hipError_t launch_gemm_bf16_planes_f32(const GemmCall& c, hipStream_t s);
 int gemm_bf16_planes_tile_n();
+
+// Skinny dense bf16 GEMM for at most 64 token rows (dense mode, no gather/scatter/SwiGLU,
+// N a multiple of 64): weight streaming split over the whole chip. The k-splits write fp32
+// partial planes to `partials` (gemm_skinny_partial_bytes; with less room it runs unsplit).
+int gemm_skinny_splits(int64_t N, int64_t K);
+size_t gemm_skinny_partial_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny(const GemmCall& c, float* partials, size_t partial_bytes, hipStream_t s);
+constexpr int64_t kSkinnyMaxRows = 64;
 
 // fp32 vector-ALU GEMM (fp32 layers and the fp32 router contraction); M-tile height 64.
 constexpr int kF32TileM = 64;

@@ -22,6 +22,8 @@
 //                   (ceil(count / BM)) -> the tile list. Experts with no tokens get no tile,
 //                   so their weights are never read.
 //   permute         one thread per copy: position = offset + block base + rank.
+//   dispatch_small  all of the above in one workgroup for batches of at most 1024 tokens,
+//                   where four launches would cost more than the work.
 // Everything here moves O(T*k) int32 words: a few MB at the largest shapes.
 #include "common.hpp"
 
@@ -172,6 +174,123 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
 
 int num_rank_blocks(int64_t T) { return static_cast<int>((T + kRankTokens - 1) / kRankTokens); }
 
+// Exclusive scan over the E <= 1024 entries v[0..E) of an LDS array by one 256-thread block
+// (four consecutive entries per thread); writes the scan to out[0..E] (out[E] = total).
+__device__ void block_exclusive_scan_e(const int32_t* v, int E, int32_t* out, int* sh) {
+  const int e0 = threadIdx.x * 4;
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    loc[q] = e0 + q < E ? v[e0 + q] : 0;
+    sum += loc[q];
+  }
+  int run = block_inclusive_scan(sum, sh) - sum;
+  __syncthreads();
+  const int total = sh[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (e0 + q < E) out[e0 + q] = run;
+    run += loc[q];
+  }
+  if (threadIdx.x == 0) out[E] = total;
+}
+
+// The whole dispatch of a small batch (T <= kSmallTokens) in one 256-thread workgroup:
+// histogram, offsets, M-tile list and stable permutation, with no intermediate global
+// buffers. Pass 1 counts with LDS atomics (exact); pass 2 walks the tokens in chunks of 256
+// in order and ranks each copy like rank_kernel (64-bit per-wavefront masks), on top of the
+// running count of its expert from the earlier chunks.
+constexpr int kSmallTokens = 1024;
+
+__global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ idx, int64_t T, int k,
+                                                             int E, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv, TileList tiles, int bm) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* bits = reinterpret_cast<uint64_t*>(smem);  // [4][E]
+  int32_t* pre = reinterpret_cast<int32_t*>(bits + 4 * E);  // [4][E]
+  int32_t* run = pre + 4 * E;                           // [E] counts, then running rank base
+  int32_t* off = run + E;                               // [E + 1] offsets
+  int32_t* mt = pre;                                    // [E] M-tiles per expert (pass 1 only)
+  int32_t* tb = pre + E;                                // [E + 1] first tile of each expert (pass 1)
+  __shared__ int sh[17];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t A = T * k;
+
+  for (int e = tid; e < E; e += 256) run[e] = 0;
+  __syncthreads();
+  for (int64_t a = tid; a < A; a += 256) {
+    const int e = idx[a];
+    if (e >= 0 && e < E) atomicAdd(&run[e], 1);
+  }
+  __syncthreads();
+  block_exclusive_scan_e(run, E, off, sh);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    counts[e] = run[e];
+    offsets[e] = off[e];
+    mt[e] = (run[e] + bm - 1) / bm;
+  }
+  if (tid == 0) offsets[E] = off[E];
+  __syncthreads();
+  if (tiles.cap > 0) {
+    block_exclusive_scan_e(mt, E, tb, sh);
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      const int c = run[e];
+      for (int i = 0; i < mt[e]; ++i) {
+        const int ti = tb[e] + i;
+        if (ti >= tiles.cap) break;
+        tiles.expert[ti] = e;
+        tiles.row0[ti] = off[e] + i * bm;
+        tiles.rows[ti] = min(bm, c - i * bm);
+      }
+    }
+    if (tid == 0) *tiles.count = min(tb[E], tiles.cap);
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += 256) run[e] = 0;
+  __syncthreads();
+
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t t0 = 0; t0 < T; t0 += 256) {
+    for (int i = tid; i < 4 * E; i += 256) bits[i] = 0;
+    __syncthreads();
+    const int64_t t = t0 + tid;
+    if (t < T) {
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[t * k + j];
+        if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]), 1ull << lane);
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      int r = run[e];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pre[w * E + e] = r;
+        r += __popcll(bits[w * E + e]);
+      }
+      run[e] = r;
+    }
+    __syncthreads();
+    if (t < T) {
+      for (int j = 0; j < k; ++j) {
+        const int64_t a = t * k + j;
+        const int e = idx[a];
+        if (e < 0 || e >= E) {
+          inv[a] = -1;
+          continue;
+        }
+        const int64_t pos = static_cast<int64_t>(off[e]) + pre[wave * E + e] + __popcll(bits[wave * E + e] & below);
+        if (pos >= 0 && pos < A) perm[pos] = static_cast<int32_t>(a);
+        inv[a] = static_cast<int32_t>(pos);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 size_t dispatch_scratch_bytes(const Layer& ly) {
@@ -184,6 +303,14 @@ hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts,
                            int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
                            int bm, hipStream_t s) {
   if (ly.T <= 0) return hipSuccess;
+  if (ly.T <= kSmallTokens) {
+    // bits [4][E] u64, pre [4][E], run [E], off [E + 1]: 56 E + 4 bytes (57 KiB at E = 1024)
+    const size_t lds = static_cast<size_t>(ly.E) * 4 * (sizeof(uint64_t) + sizeof(int32_t)) +
+                       static_cast<size_t>(2 * ly.E + 1) * sizeof(int32_t);
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), lds, s, idx, ly.T, ly.k, ly.E, counts, offsets,
+                       perm, inv, tiles, bm);
+    return hipGetLastError();
+  }
   const int nblk = num_rank_blocks(ly.T);
   const int64_t A = ly.T * ly.k;
   int32_t* rank = static_cast<int32_t*>(scratch);

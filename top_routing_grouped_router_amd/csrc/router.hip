@@ -18,16 +18,17 @@
 // exactly into three bf16 planes (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid):
 // 24 significant bits between them); x is bf16, so every product x * plane is exact in fp32
 // and the three MFMA products accumulate in fp32 -- an fp32-accurate dot product (3*d terms)
-// at bf16 matrix rate. Tile 64 tokens x 64 experts x 64 k, four wavefronts of 32 x 32 on
-// v_mfma_f32_16x16x32_bf16. The contraction can be split over `nsplit` workgroups along
-// d_model for occupancy; the partial sums land in separate planes and the gate kernel adds
-// them in a fixed order, so the result is deterministic.
+// at bf16 matrix rate. Tile 64 tokens x 64 experts x 64 k (four wavefronts of 32 x 32), or
+// 64 tokens x 16 experts for few tokens and many experts, on v_mfma_f32_16x16x32_bf16. The
+// contraction can be split over `nsplit` workgroups along d_model for occupancy; the partial
+// sums land in separate planes and the gate kernel adds them in a fixed order, so the result
+// is deterministic.
 //
 // gate_topk: one 64-lane wavefront per token; each lane holds ceil(E/64) <= 16 experts in
-// registers (the count is a template parameter). Selection is k rounds of a wave-wide arg-max over a 64-bit key
-// (order-preserving bits of the key, then the complemented expert index), so each round is
-// six xor-shuffle steps and the result is exact and deterministic. The logits row is read
-// once, coalesced; the kernel is bound by HBM/L2 reads of the logits.
+// registers (the count is a template parameter). Selection is k rounds of a wave-wide
+// arg-max: the largest order-preserving key code through DPP row reductions and scalar
+// readlanes, the owning lane from a ballot (ties across lanes: the lowest expert index), so
+// the result is exact and deterministic. The logits row is read once, coalesced.
 #include <math.h>
 
 #include <algorithm>
@@ -70,7 +71,6 @@ struct GateArgs {
 
 template <int GATING, bool FROM_SCORES, int PL>
 __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
-  constexpr int kMaxPerLane = PL;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;  // whole wavefront leaves together
@@ -78,34 +78,44 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   const int64_t plane = a.T * static_cast<int64_t>(E);
   const float* row = a.in + t * E;
 
-  float v[kMaxPerLane];  // logits (or the given gating output)
-  float s[kMaxPerLane];  // gating scores (unused for topk_softmax weights)
+  // Logits (or the given gating output): plane 0, then the other partial-sum planes added in
+  // plane order. The plane loop is outermost so each batch issues PB * PL independent loads.
+  // Padding slots (e >= E) load the last expert's value (clamped index: every load is in
+  // bounds and unconditional) and are masked below.
+  float v[PL];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) v[i] = row[min(i * kWave + lane, E - 1)];
+  constexpr int PB = PL >= 8 ? 2 : 4;  // planes per batch
+  for (int p0 = 1; p0 < a.nsplit; p0 += PB) {
+    float pv[PB][PL];
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        pv[u][i] = row[min(p0 + u, a.nsplit - 1) * plane + min(i * kWave + lane, E - 1)];
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+      if (p0 + u < a.nsplit) {
+#pragma unroll
+        for (int i = 0; i < PL; ++i) v[i] += pv[u][i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
     const int e = i * kWave + lane;
     if (e < E) {
-      // Partial planes summed in plane order; loaded eight at a time so the loads overlap.
-      float acc = row[e];
-      for (int p0 = 1; p0 < a.nsplit; p0 += 8) {
-        float pv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pv[u] = (p0 + u < a.nsplit) ? row[(p0 + u) * plane + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (p0 + u < a.nsplit) acc += pv[u];
-      }
-      if (!FROM_SCORES && a.router_bias) acc += a.router_bias[e];
-      v[i] = acc;
-      if (!FROM_SCORES && a.logits_out) a.logits_out[t * E + e] = acc;
+      if (!FROM_SCORES && a.router_bias) v[i] += a.router_bias[e];
+      if (!FROM_SCORES && a.logits_out) a.logits_out[t * E + e] = v[i];
     } else {
       v[i] = -INFINITY;
     }
   }
 
+  float s[PL];  // gating scores
   if (!FROM_SCORES) {
     if (GATING == MOE_GATING_SIGMOID) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
+      for (int i = 0; i < PL; ++i) {
         float sc = 1.f / (1.f + expf(-v[i]));
         if (a.sig_eps != 0.f) sc = sc + a.sig_eps;
         s[i] = sc;
@@ -113,58 +123,80 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
     } else {
       float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, v[i]);
-      m = wave_max(m);
+      for (int i = 0; i < PL; ++i) m = fmaxf(m, v[i]);
+      m = wave_max_f32_dpp(m);
       float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
+      for (int i = 0; i < PL; ++i) {
         const int e = i * kWave + lane;
         s[i] = (e < E) ? expf(v[i] - m) : 0.f;
         sum += s[i];
       }
-      sum = wave_sum(sum);
+      sum = wave_sum_f32_dpp(sum);
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) s[i] = s[i] / sum;
+      for (int i = 0; i < PL; ++i) s[i] = s[i] / sum;
     }
     if (a.scores_out) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i) {
+      for (int i = 0; i < PL; ++i) {
         const int e = i * kWave + lane;
         if (e < E) a.scores_out[t * E + e] = s[i];
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) s[i] = v[i];
+    for (int i = 0; i < PL; ++i) s[i] = v[i];
   }
 
-  // 64-bit candidates: (key code << 32) | ~expert. Max = largest key, then lowest index.
-  uint64_t cand[kMaxPerLane];
+  // Selection keys as order-preserving codes; 0 marks "no candidate" (padding, or chosen).
+  uint32_t code[PL];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) {
     const int e = i * kWave + lane;
-    if (e < E) {
-      float key = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[i] : s[i];
-      if (a.score_bias) key = key + a.score_bias[e];
-      cand[i] = (static_cast<uint64_t>(key_code(key)) << 32) | static_cast<uint32_t>(~e);
-    } else {
-      cand[i] = 0;
-    }
+    float key = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[i] : s[i];
+    if (a.score_bias) key = key + a.score_bias[min(e, E - 1)];
+    code[i] = e < E ? key_code(key) : 0u;
   }
 
+  // k rounds. A lane's own best is its largest code, first slot on ties (lane l holds experts
+  // l, l+64, ..., so the first slot is its lowest index). The wave maximum code is found with
+  // DPP; usually one lane holds it and its best is the pick. When several lanes tie at the
+  // maximum, the lowest expert index among their bests wins. The pick's weight source (score,
+  // or logit for topk_softmax) comes from the owning lane's register by readlane.
   int my_sel = 0;
+  float my_val = 0.f;
   for (int j = 0; j < a.k; ++j) {
-    uint64_t best = 0;
+    uint32_t best = 0;
+    int bslot = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) best = cand[i] > best ? cand[i] : best;
-    best = wave_max_u64(best);
-    int e = static_cast<int>(~static_cast<uint32_t>(best));
+    for (int i = 0; i < PL; ++i)
+      if (code[i] > best) {
+        best = code[i];
+        bslot = i;
+      }
+    float bval = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[0] : s[0];
+#pragma unroll
+    for (int i = 1; i < PL; ++i)
+      if (bslot == i) bval = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[i] : s[i];
+    const uint32_t m = wave_max_u32_dpp(best);
+    const uint64_t ball = __ballot(best == m);
+    int e;
+    if (__popcll(ball) == 1) {
+      const int wl = __ffsll(static_cast<unsigned long long>(ball)) - 1;
+      e = __builtin_amdgcn_readlane(bslot, wl) * kWave + wl;
+    } else {
+      e = wave_min_i32_dpp(best == m ? bslot * kWave + lane : 0x7fffffff);
+    }
     e = min(max(e, 0), E - 1);  // k <= E, so a candidate always exists
-    if (lane == j) my_sel = e;
+    const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bval), e & (kWave - 1)));
+    if (lane == j) {
+      my_sel = e;
+      my_val = val;
+    }
     if (lane == (e & (kWave - 1))) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
-        if (i == (e >> 6)) cand[i] = 0;
+      for (int i = 0; i < PL; ++i)
+        if (i == (e >> 6)) code[i] = 0;
     }
   }
 
@@ -172,39 +204,23 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   const bool active = lane < a.k;
   float w;
   if (GATING == MOE_GATING_TOPK_SOFTMAX) {
-    // the selected expert's logit, from the register of its owning lane
-    const int src = my_sel & (kWave - 1), slot = my_sel >> 6;
-    float lv = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const float sv = __shfl(v[i], src, kWave);
-      if (i == slot) lv = sv;
-    }
-    if (!active) lv = -INFINITY;
-    const float m = wave_max(lv);
+    const float lv = active ? my_val : -INFINITY;
+    const float m = wave_max_f32_dpp(lv);
     const float ex = active ? expf(lv - m) : 0.f;
-    const float sum = wave_sum(ex);
+    const float sum = wave_sum_f32_dpp(ex);
     w = ex / sum;
   } else {
-    // Fetch the exact score register of the selected expert from its owning lane.
-    const int src = my_sel & (kWave - 1), slot = my_sel >> 6;
-    w = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const float sv = __shfl(s[i], src, kWave);
-      if (i == slot) w = sv;
-    }
-    if (!active) w = 0.f;
+    w = active ? my_val : 0.f;
   }
   if (a.norm_p != 0.f) {
     const float aw = active ? fabsf(w) : 0.f;
     float nrm;
     if (a.norm_p == 1.f) {
-      nrm = wave_sum(aw);
+      nrm = wave_sum_f32_dpp(aw);
     } else if (a.norm_p == 2.f) {
-      nrm = sqrtf(wave_sum(aw * aw));
+      nrm = sqrtf(wave_sum_f32_dpp(aw * aw));
     } else {
-      nrm = powf(wave_sum(active ? powf(aw, a.norm_p) : 0.f), 1.f / a.norm_p);
+      nrm = powf(wave_sum_f32_dpp(active ? powf(aw, a.norm_p) : 0.f), 1.f / a.norm_p);
     }
     w = w / nrm;
   }
@@ -242,12 +258,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRT = 64;    // tokens per tile
-constexpr int kRE = 64;    // experts per tile
 constexpr int kRBK = 64;   // k per stage
 constexpr int kRowB = kRBK * 2;
 constexpr int kXBytes = kRT * kRowB;        // 8 KiB
-constexpr int kPlaneBytes = kRE * kRowB;    // 8 KiB per bf16 plane
-constexpr int kRStage = kXBytes + 3 * kPlaneBytes;
+
+// Expert tiles of the split-K router: 64 experts (2 x 2 wavefronts of 32 tokens x 32 experts)
+// when the tokens alone give enough tiles; 16 experts (4 wavefronts of 16 tokens x 16 experts)
+// for few tokens, so that a wide expert pool fills the chip with 4x fewer k-splits (fewer
+// partial planes for the gate kernel to add).
+template <int RE_>
+struct RouterTile {
+  static constexpr int RE = RE_;
+  static constexpr int WN = RE >= 64 ? 2 : 1;   // wavefronts along experts
+  static constexpr int WM = 4 / WN;             // wavefronts along tokens
+  static constexpr int TI = kRT / (16 * WM);    // 16-token sub-tiles per wavefront
+  static constexpr int TJ = RE / (16 * WN);     // 16-expert sub-tiles per wavefront
+  static constexpr int kPlaneBytes = RE * kRowB;
+  static constexpr int kStage = kXBytes + 3 * kPlaneBytes;
+  static constexpr int NWQ = RE * 16 / 256;     // 16-byte fp32 weight chunks per thread per stage
+  static_assert(WM * WN == 4 && TI >= 1 && TJ >= 1 && NWQ >= 1, "router tile");
+};
 
 // 16-lane passes over 16 consecutive rows: slot = chunk ^ ((row >> 1) & 7) spreads them over
 // all 64 LDS banks (a 128-byte row covers half of them).
@@ -287,15 +317,16 @@ __global__ __launch_bounds__(256) void split_planes_kernel(const float4* __restr
   }
 }
 
+template <class RT>
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ Wr,
                                                           float* __restrict__ part, int64_t T, int E,
                                                           int d, int nsplit) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kRStage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * RT::kStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 wavefronts of 32 tokens x 32 experts
+  const int wm = wave / RT::WN, wn = wave % RT::WN;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRT;
-  const int e0 = blockIdx.y * kRE;
+  const int e0 = blockIdx.y * RT::RE;
   const int sp = blockIdx.z;
   const int nk = d / kRBK;
   const int kb = static_cast<int>(static_cast<int64_t>(sp) * nk / nsplit);
@@ -303,7 +334,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 
   const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
   const unsigned char* wb = reinterpret_cast<const unsigned char*>(Wr);
-  uint32_t xoff[2], woff[4];
+  uint32_t xoff[2], woff[RT::NWQ];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int c = tid + 256 * q, row = c >> 3, ch = c & 7;
@@ -311,31 +342,31 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     xoff[q] = static_cast<uint32_t>((t * d + ch * 8) * 2);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < RT::NWQ; ++q) {
     const int c = tid + 256 * q, row = c >> 4, c4 = c & 15;
     const int64_t e = min(e0 + row, E - 1);
     woff[q] = static_cast<uint32_t>((e * d + c4 * 4) * 4);
   }
 
   u32x4 rx[2];
-  f32x4 rw[4];
+  f32x4 rw[RT::NWQ];
   auto gload = [&](int kt) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       rx[q] = *reinterpret_cast<const u32x4*>(xb + (xoff[q] + static_cast<uint32_t>(kt) * kRowB));
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < RT::NWQ; ++q)
       rw[q] = *reinterpret_cast<const f32x4*>(wb + (woff[q] + static_cast<uint32_t>(kt) * (kRBK * 4)));
   };
   auto sstore = [&](int buf) {
-    unsigned char* base = lds + buf * kRStage;
+    unsigned char* base = lds + buf * RT::kStage;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int c = tid + 256 * q;
       *reinterpret_cast<u32x4*>(base + rswz(c >> 3, c & 7)) = rx[q];
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < RT::NWQ; ++q) {
       const int c = tid + 256 * q, row = c >> 4, c4 = c & 15;
       uint16_t hi[4], mi[4], lo[4];
 #pragma unroll
@@ -343,16 +374,16 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
       const int off = rswz(row, c4 >> 1) + (c4 & 1) * 8;
       unsigned char* pl = base + kXBytes;
       *reinterpret_cast<uint2*>(pl + off) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-      *reinterpret_cast<uint2*>(pl + kPlaneBytes + off) = make_uint2(pack2(mi[0], mi[1]), pack2(mi[2], mi[3]));
-      *reinterpret_cast<uint2*>(pl + 2 * kPlaneBytes + off) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+      *reinterpret_cast<uint2*>(pl + RT::kPlaneBytes + off) = make_uint2(pack2(mi[0], mi[1]), pack2(mi[2], mi[3]));
+      *reinterpret_cast<uint2*>(pl + 2 * RT::kPlaneBytes + off) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
     }
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[RT::TI][RT::TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RT::TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RT::TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (kb < ke) {
     gload(kb);
@@ -361,25 +392,25 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     for (int kt = kb; kt < ke; ++kt) {
       const int buf = (kt - kb) & 1;
       if (kt + 1 < ke) gload(kt + 1);
-      const unsigned char* X = lds + buf * kRStage;
+      const unsigned char* X = lds + buf * RT::kStage;
       const unsigned char* Wp = X + kXBytes;
 #pragma unroll
       for (int s32 = 0; s32 < 2; ++s32) {
         const int ch = 4 * s32 + (lane >> 4);
-        bf16x8 xf[2], wf[3][2];
+        bf16x8 xf[RT::TI], wf[3][RT::TJ];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          xf[i] = *reinterpret_cast<const bf16x8*>(X + rswz(32 * wm + 16 * i + (lane & 15), ch));
+        for (int i = 0; i < RT::TI; ++i)
+          xf[i] = *reinterpret_cast<const bf16x8*>(X + rswz(16 * (RT::TI * wm + i) + (lane & 15), ch));
 #pragma unroll
         for (int p = 0; p < 3; ++p)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            wf[p][j] = *reinterpret_cast<const bf16x8*>(Wp + p * kPlaneBytes +
-                                                       rswz(32 * wn + 16 * j + (lane & 15), ch));
+          for (int j = 0; j < RT::TJ; ++j)
+            wf[p][j] = *reinterpret_cast<const bf16x8*>(Wp + p * RT::kPlaneBytes +
+                                                       rswz(16 * (RT::TJ * wn + j) + (lane & 15), ch));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < RT::TI; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < RT::TJ; ++j)
 #pragma unroll
             for (int p = 2; p >= 0; --p)
               acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[p][j], xf[i], acc[i][j], 0, 0, 0);
@@ -392,18 +423,41 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   // Lane holds token (lane & 15) of each 16-token sub-tile and experts 4*(lane >> 4) + r.
   float* out = part + static_cast<int64_t>(sp) * T * E;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t t = t0 + 32 * wm + 16 * i + (lane & 15);
+  for (int i = 0; i < RT::TI; ++i) {
+    const int64_t t = t0 + 16 * (RT::TI * wm + i) + (lane & 15);
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < RT::TJ; ++j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int e = e0 + 32 * wn + 16 * j + 4 * (lane >> 4) + r;
+        const int e = e0 + 16 * (RT::TJ * wn + j) + 4 * (lane >> 4) + r;
         if (e < E) out[t * E + e] = acc[i][j][r];
       }
     }
   }
+}
+
+// Expert-tile width of the split-K router for this layer (RouterTile<RE>) and its k-splits.
+struct RouterPlan {
+  int re;
+  int splits;
+};
+
+RouterPlan router_plan(const Layer& ly) {
+  const int nk = static_cast<int>(ly.d / kRBK);
+  const int64_t tm = (ly.T + kRT - 1) / kRT;
+  RouterPlan p{64, 1};
+  int64_t tiles = tm * ((ly.E + 63) / 64);
+  int64_t target = 512;
+  if (ly.E > 64 && tiles * 8 < 512) {  // few tokens, wide pool: narrow expert tiles
+    p.re = 16;
+    tiles = tm * ((ly.E + 15) / 16);
+    target = 384;
+  }
+  // enough workgroups to cover the chip (a fixed target, so the workspace size does not
+  // depend on the device), each keeping at least one k-stage
+  while (p.splits * 2 <= nk && p.splits < 32 && tiles * p.splits < target) p.splits *= 2;
+  return p;
 }
 
 }  // namespace
@@ -422,13 +476,7 @@ size_t router_scratch_bytes(const Layer& ly) {
 
 int router_splits(const Layer& ly) {
   if (!ly.bf16 || router_uses_planes(ly)) return 1;
-  const int64_t tiles = ((ly.T + kRT - 1) / kRT) * ((ly.E + kRE - 1) / kRE);
-  const int nk = static_cast<int>(ly.d / kRBK);
-  int s = 1;
-  // enough workgroups to cover the chip (a fixed target, so the workspace size does not
-  // depend on the device), each keeping at least one k-stage
-  while (s * 2 <= nk && s < 32 && tiles * s < 512) s *= 2;
-  return s;
+  return router_plan(ly).splits;
 }
 
 hipError_t launch_gate_topk(const Layer& ly, const float* input, int nsplit, bool from_scores,
@@ -487,10 +535,15 @@ hipError_t launch_router_logits(const Layer& ly, const void* x, const float* Wr,
     return launch_gemm_bf16_planes_f32(c, s);
   }
   if (ly.bf16) {
-    const dim3 g(static_cast<unsigned>((ly.T + kRT - 1) / kRT), static_cast<unsigned>((ly.E + kRE - 1) / kRE),
+    const RouterPlan p = router_plan(ly);
+    const dim3 g(static_cast<unsigned>((ly.T + kRT - 1) / kRT), static_cast<unsigned>((ly.E + p.re - 1) / p.re),
                  static_cast<unsigned>(nsplit));
-    hipLaunchKernelGGL(router_mfma_kernel, g, dim3(256), 0, s, static_cast<const uint16_t*>(x), Wr, partials,
-                       ly.T, ly.E, static_cast<int>(ly.d), nsplit);
+    if (p.re == 16)
+      hipLaunchKernelGGL(router_mfma_kernel<RouterTile<16>>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x), Wr,
+                         partials, ly.T, ly.E, static_cast<int>(ly.d), nsplit);
+    else
+      hipLaunchKernelGGL(router_mfma_kernel<RouterTile<64>>, g, dim3(256), 0, s, static_cast<const uint16_t*>(x), Wr,
+                         partials, ly.T, ly.E, static_cast<int>(ly.d), nsplit);
     return hipGetLastError();
   }
   GemmCall c{};
