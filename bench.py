@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference the HBM "
                          "byte counters are scaled by")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: write profiles/expert_gemm_traffic_<workload>.json from four rocprofv3 "
+                         "--pmc output folders (FETCH_SIZE and WRITE_SIZE of this bench, then of "
+                         "--copy-calibration 256)")
     return ap.parse_args()
 
 
@@ -81,6 +85,74 @@ def event_time_ms(fn, n, torch):
     return sum(a.elapsed_time(b) for a, b in evs) / n
 
 
+def _counter_rows(folder):
+    """(kernel name, counter value) per dispatch from a rocprofv3 --pmc csv output folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    with open(files[0]) as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
+
+
+def _mean(vals):
+    if not vals:
+        raise SystemExit("counter record: kernel not found in the profile")
+    return sum(vals) / len(vals)
+
+
+def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib=256):
+    """HBM bytes per expert-stage launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the two
+    expert GEMM kernels, each scaled by what the same counter reads for a plain device copy of
+    copy_mib MiB. Written with the hash of the kernel sources, so that a later change of the
+    kernels voids the record."""
+    def gemm_kind(name):
+        if "gemm_bf16_kernel" not in name:
+            return None
+        tail = name.split(">", 1)[1] if ">" in name else name
+        flags = [t.strip() for t in tail.split(",")][1:4]
+        if flags[:3] == ["true", "true", "false"]:
+            return "gemm1"
+        if flags[:3] == ["false", "false", "true"]:
+            return "gemm2"
+        return None
+
+    def per_kernel(folder):
+        out = {"gemm1": [], "gemm2": []}
+        for name, v in _counter_rows(folder):
+            kind = gemm_kind(name)
+            if kind:
+                out[kind].append(v)
+        return {k: _mean(v) for k, v in out.items()}
+
+    def copy_kib(folder):
+        vals = sorted((v for name, v in _counter_rows(folder) if "copyBuffer" in name), reverse=True)
+        return _mean(vals[:3])
+
+    copied = float(copy_mib << 10)
+    cf, cw = copy_kib(copy_fetch_dir), copy_kib(copy_write_dir)
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    fs, ws = copied / cf, copied / cw
+    total = sum(fetch.values()) * fs * 1024 + sum(write.values()) * ws * 1024
+    rec = {
+        "workload": workload,
+        "kernels": "gemm_bf16 GEMM1 (up/gate + SwiGLU, gathered A) + GEMM2 (down, scattered C), "
+                   "one launch each per stage",
+        "source_sha256": kernel_source_sha256(),
+        "source_files": list(GEMM_SOURCES),
+        "fetch_size_kib_per_launch": fetch,
+        "write_size_kib_per_launch": write,
+        "copy_calibration": {"bytes_copied_kib": copied, "fetch_size_kib": cf, "write_size_kib": cw,
+                             "fetch_scale": fs, "write_scale": ws},
+        "bytes_per_launch": int(round(total)),
+    }
+    path = os.path.join(ROOT, "profiles", f"expert_gemm_traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(cfg, w, x, n_tokens):
     import numpy as np
     import workloads
@@ -104,6 +176,9 @@ def cpu_baseline(cfg, w, x, n_tokens):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
