@@ -31,13 +31,18 @@ Readings where the pages are silent (each is listed with its reason in the desig
   * latent restore order: combine, then RMSNorm(eps, weight g, no bias), cast, up-projection;
   * down/up projections carry no bias; all weights are stored (out_features, in_features).
 
+Balancing state ([OC3 "Счётчики и bias-корректировка"]): the count accumulator, the load
+imbalance metric max/mean, and the score_bias update by bias_gamma * sign(ideal - actual).
+
 Pins (tests/test_oracle_pins.py): parameter counts against the element counts of the
 generated tensors and the golden table; logits against an exactly-rounded fsum dot
 product; gating against torch's softmax/sigmoid; selection against brute force over all
 k-subsets and against Python's sort; weights against closed forms (golden fixtures);
 histogram/permutation against invariants and a brute-force counting sort; the expert path
 against a dense evaluation of every expert on every token; special cases against torch's
-silu / rms_norm; permutation equivariance and RMSNorm scale invariance.
+silu / rms_norm; permutation equivariance and RMSNorm scale invariance; the balancing
+state against closed forms (uniform load, one hot expert, fractional ideal) and against
+exact rational arithmetic (fractions.Fraction) on random counts.
 """
 from __future__ import annotations
 
@@ -349,6 +354,41 @@ def forward(cfg: MoEConfig, weights: dict, x) -> dict:
     out["o"] = o
     out.update(restore_routed_output(cfg, o, weights.get("norm_weight"), weights.get("up_proj")))
     return out
+
+
+# ------------------------------------------------------------------- balancing state
+
+def accumulate_counts(accumulator, counts) -> np.ndarray:
+    """[OC3 "Счётчики и bias-корректировка"]: score_bias_batch_size_per_expert accumulates
+    the number of tokens assigned to each expert over the step's forward passes (it is summed
+    into, then reset after the step). Integer add."""
+    return np.asarray(accumulator, dtype=np.int64) + np.asarray(counts, dtype=np.int64)
+
+
+def load_imbalance(counts) -> float:
+    """[OC3 "Счётчики и bias-корректировка"]: the load imbalance metric is the maximum of the
+    per-expert counter divided by its mean. mean = total / E, so the ratio is max * E / total,
+    formed as one float64 division of the two exact integers (correctly rounded). With no
+    tokens the mean is 0 and the ratio 0/0: NaN. The cross-process aggregations the page
+    names (max for the local metric, mean for the global one) combine values of this same
+    function."""
+    c = np.asarray(counts, dtype=np.int64)
+    total = int(c.sum())
+    if total == 0:
+        return float("nan")
+    return float(int(c.max()) * c.size) / float(total)
+
+
+def score_bias_update(score_bias, accumulator, bias_gamma: float) -> np.ndarray:
+    """[OC3 "Счётчики и bias-корректировка"] and [OC3 "Управление состоянием между шагами"]:
+    after the step, the ideal mean size per expert is computed from the accumulated counts,
+    score_bias moves by bias_gamma * sign(ideal - actual), and the accumulator is reset (the
+    caller's job here). ideal = total / E; the sign is taken exactly, as sign(total - E *
+    actual) in integers. The move is one fp32 add of +-bias_gamma or 0 to the fp32 bias."""
+    c = np.asarray(accumulator, dtype=np.int64)
+    sgn = np.sign(int(c.sum()) - c.size * c).astype(np.float32)
+    step = np.float32(bias_gamma) * sgn
+    return (np.asarray(score_bias, dtype=np.float32) + step).astype(np.float32)
 
 
 # ------------------------------------------------------------------- parameter counts

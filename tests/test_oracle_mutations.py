@@ -92,3 +92,31 @@ def test_planted_mistake_is_caught(monkeypatch, target, bad, pin):
     monkeypatch.setattr(O, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+def _bias_sign_reversed(score_bias, accumulator, bias_gamma):
+    c = np.asarray(accumulator, dtype=np.int64)
+    sgn = np.sign(c.size * c - int(c.sum())).astype(np.float32)  # actual - ideal
+    return (np.asarray(score_bias, np.float32) + np.float32(bias_gamma) * sgn).astype(np.float32)
+
+
+def _imbalance_mean_of_used_experts(counts):
+    c = np.asarray(counts, dtype=np.int64)
+    used = c[c > 0]
+    if used.size == 0:
+        return float("nan")
+    return float(int(used.max()) * used.size) / float(int(used.sum()))  # mean over used experts only
+
+
+BALANCE_MUTATIONS = [
+    ("score_bias_update", _bias_sign_reversed, lambda: P.test_score_bias_update_closed_forms()),
+    ("load_imbalance", _imbalance_mean_of_used_experts, lambda: P.test_load_imbalance_closed_forms()),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", BALANCE_MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in BALANCE_MUTATIONS])
+def test_planted_balance_mistake_is_caught(monkeypatch, target, bad, pin):
+    monkeypatch.setattr(O, target, bad)
+    with pytest.raises(AssertionError):
+        pin()

@@ -367,3 +367,77 @@ def test_counts_feed_offsets_and_perm_on_full_layer():
     assert out["counts"].sum() == 64 * 4
     for t in range(64):
         assert len(set(out["idx"][t].tolist())) == 4
+
+
+# ----------------------------------------------------------------- balancing state
+# [OC3 "Счётчики и bias-корректировка"]: load imbalance = max / mean of the per-expert counter;
+# score_bias += bias_gamma * sign(ideal - actual) with ideal the mean size per expert.
+
+from fractions import Fraction  # noqa: E402
+
+BALANCE_E = (1, 2, 7, 64, 256, 896, 1024)
+BALANCE_KINDS = ("uniform", "hot", "zipf", "random", "sparse")
+
+
+def test_load_imbalance_closed_forms():
+    assert O.load_imbalance(workloads.synthetic_counts(64, "uniform")) == 1.0
+    for E in (1, 8, 896):
+        assert O.load_imbalance(workloads.synthetic_counts(E, "hot")) == float(E)
+    assert O.load_imbalance([1, 2]) == 4.0 / 3.0  # max 2, mean 3/2
+    assert O.load_imbalance([0, 0, 3]) == 3.0
+    assert np.isnan(O.load_imbalance(workloads.synthetic_counts(16, "zero")))
+
+
+@pytest.mark.parametrize("E", BALANCE_E)
+@pytest.mark.parametrize("kind", BALANCE_KINDS)
+def test_load_imbalance_is_exact_ratio(E, kind):
+    c = workloads.synthetic_counts(E, kind, seed=3)
+    if c.sum() == 0:
+        return
+    mean = Fraction(int(c.sum()), E)
+    assert O.load_imbalance(c) == float(Fraction(int(c.max())) / mean)  # correctly rounded
+
+
+def test_score_bias_update_closed_forms():
+    g = np.float32(0.125)
+    b = np.array([0.5, -1.0, 3.0, 0.25], dtype=np.float32)
+    # uniform load: actual == ideal everywhere, sign 0, bias unchanged
+    assert np.array_equal(O.score_bias_update(b, [7, 7, 7, 7], g), b)
+    # all tokens on expert 2: it moves down by gamma, every other expert up by gamma
+    want = np.array([0.625, -0.875, 2.875, 0.375], dtype=np.float32)
+    assert np.array_equal(O.score_bias_update(b, [0, 0, 40, 0], g), want)
+    # ideal 1.5 is fractional: 1 < 1.5 up, 2 > 1.5 down
+    assert np.array_equal(O.score_bias_update(np.zeros(2, np.float32), [1, 2], 0.5),
+                          np.array([0.5, -0.5], dtype=np.float32))
+    # a single expert always holds the ideal load
+    assert np.array_equal(O.score_bias_update(np.array([2.0], np.float32), [12345], 1.0),
+                          np.array([2.0], np.float32))
+    # no tokens: every expert at the ideal 0
+    assert np.array_equal(O.score_bias_update(b, [0, 0, 0, 0], g), b)
+
+
+@pytest.mark.parametrize("E", BALANCE_E)
+@pytest.mark.parametrize("kind", BALANCE_KINDS)
+def test_score_bias_update_against_rational_sign(E, kind):
+    c = workloads.synthetic_counts(E, kind, seed=5)
+    b = (np.random.default_rng(E).standard_normal(E) * 0.1).astype(np.float32)
+    g = 1e-3
+    ideal = Fraction(int(c.sum()), E)
+    got = O.score_bias_update(b, c, g)
+    for e in range(E):
+        d = ideal - int(c[e])
+        step = np.float32(g) if d > 0 else (-np.float32(g) if d < 0 else np.float32(0))
+        assert got[e] == np.float32(b[e] + step), e
+    # the move is at most one fp32 gamma, plus the rounding of the fp32 sum
+    assert np.all(np.abs(got.astype(np.float64) - b) <= float(np.float32(g)) + np.spacing(np.abs(got)))
+
+
+def test_accumulated_counts_equal_counts_of_all_batches():
+    rng = np.random.default_rng(11)
+    E, k = 64, 4
+    batches = [np.stack([rng.permutation(E)[:k] for _ in range(T)]) for T in (5, 17, 1, 40)]
+    acc = np.zeros(E, dtype=np.int64)
+    for idx in batches:
+        acc = O.accumulate_counts(acc, O.expert_counts(idx, E))
+    every = np.concatenate([b.ravel() for b in batches])
+    assert np.array_equal(acc, np.array([np.sum(every == e) for e in range(E)]))

@@ -219,3 +219,29 @@ def random_distinct_indices(T: int, E: int, k: int, device="cpu", seed: int = 0,
         p = torch.arange(1, E + 1, device=device, dtype=torch.float64) ** (-skew)
         key = key / p
     return torch.topk(key, k, dim=1).indices.to(torch.int32)
+
+
+def synthetic_counts(num_experts: int, kind: str, seed: int = 0, total: int = 65536) -> np.ndarray:
+    """Per-expert token counts (int64) for the balancing-state checks: 'uniform' (all equal,
+    total rounded down to a multiple of E), 'hot' (all tokens on expert E // 2), 'zipf'
+    (counts proportional to 1/(e+1), rounded down), 'random' (uniform integers in
+    [0, 2*total/E]), 'sparse' (random with about half the experts at zero), 'zero'."""
+    E = num_experts
+    rng = np.random.default_rng(np.random.SeedSequence([seed, E, len(kind)]))
+    if kind == "uniform":
+        return np.full(E, total // E, dtype=np.int64)
+    if kind == "hot":
+        c = np.zeros(E, dtype=np.int64)
+        c[E // 2] = total
+        return c
+    if kind == "zipf":
+        return np.floor(total / (np.arange(E) + 1.0) / np.sum(1.0 / (np.arange(E) + 1.0))).astype(np.int64)
+    if kind == "random":
+        return rng.integers(0, 2 * max(total // E, 1) + 1, size=E).astype(np.int64)
+    if kind == "sparse":
+        c = rng.integers(0, 2 * max(total // E, 1) + 1, size=E).astype(np.int64)
+        c[rng.random(E) < 0.5] = 0
+        return c
+    if kind == "zero":
+        return np.zeros(E, dtype=np.int64)
+    raise ValueError(kind)
