@@ -46,7 +46,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
 
@@ -262,6 +262,37 @@ MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const moe_weights_t* w
 MOE_API moe_status_t moe_latent_up(const moe_config_t* cfg, const moe_weights_t* weights,
                            int64_t num_tokens, const void* n, void* y, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* ------------------------------------------------------------------------ balancing state */
+
+/*
+ * Router load-balancing state ([OC3 "Счётчики и bias-корректировка"], [OC3 "Управление
+ * состоянием между шагами"]). Counters are per-expert int64 device arrays of num_experts
+ * entries (1..MOE_MAX_EXPERTS) owned by the caller; everything is integer arithmetic apart
+ * from the two results named below, and nothing depends on reduction order.
+ */
+
+/* accumulator (E) int64 += batch_size_per_expert (E) int32 -- the step's
+ * score_bias_batch_size_per_expert accumulator, fed with the counts of each forward
+ * (moe_routing_t.batch_size_per_expert). INVALID_ARG on NULL pointers or E out of range. */
+MOE_API moe_status_t moe_accumulate_expert_counts(int32_t num_experts, const int32_t* batch_size_per_expert,
+                                                  int64_t* accumulator, void* stream);
+
+/* Load imbalance of a counter: max(counts) / mean(counts) = max * E / total, one fp64 division
+ * of the exact integers (correctly rounded), written to *imbalance (one double on the device).
+ * No tokens (total 0): NaN, the value of 0 / 0. The page aggregates the local metric over
+ * processes with max and the global one with mean; one process computes this value once. */
+MOE_API moe_status_t moe_load_imbalance(int32_t num_experts, const int64_t* counts, double* imbalance,
+                                        void* stream);
+
+/* The aux-loss-free score_bias update, run once per step: with ideal = total / E the mean
+ * size per expert, score_bias[e] (fp32, in place) += bias_gamma * sign(ideal - accumulator[e])
+ * (the sign taken exactly, in integers; one fp32 add of +-bias_gamma or 0), then the
+ * accumulator is zeroed. imbalance may be NULL; otherwise it receives the load imbalance of
+ * the accumulator before the reset. INVALID_ARG on NULL required pointers, E out of range or
+ * a non-finite bias_gamma. */
+MOE_API moe_status_t moe_score_bias_update(int32_t num_experts, float bias_gamma, int64_t* accumulator,
+                                           float* score_bias, double* imbalance, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,8 @@ def test_header_declares_the_abi():
                  "moe_experts_forward", "moe_combine", "moe_latent_down", "moe_latent_up",
                  "moe_config_default", "moe_config_validate", "moe_num_params",
                  "moe_workspace_size", "moe_status_string", "moe_last_error_message",
-                 "moe_abi_version"):
+                 "moe_abi_version", "moe_accumulate_expert_counts", "moe_load_imbalance",
+                 "moe_score_bias_update"):
         assert name in syms
 
 
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_size():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     c = moe._CConfig()
     assert moe._config_default(ctypes.byref(c)) == 0
     assert c.struct_size == ctypes.sizeof(moe._CConfig)
@@ -143,3 +144,21 @@ def test_forward_argument_errors_before_any_gpu_call():
     assert moe._latent_down(ctypes.byref(lat), ctypes.byref(wl), T, fake, fake, fake, need_l - 1, None) == 3
     assert moe._latent_up(ctypes.byref(lat), ctypes.byref(wl), T, fake, fake, fake, need_l - 1, None) == 3
     assert moe._permute(ctypes.byref(c), T, fake, fake, fake, fake, fake, fake, 16, None) == 3
+
+
+def test_balancing_entry_points_validate_before_any_gpu_call():
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+    for E in (0, -1, 1025):
+        assert moe._accumulate_counts(E, fake, fake, None) == 1
+        assert moe._load_imbalance(E, fake, fake, None) == 1
+        assert moe._score_bias_update(E, 0.1, fake, fake, None, None) == 1
+        assert "num_experts" in moe._last_error().decode()
+    assert moe._accumulate_counts(8, None, fake, None) == 1
+    assert moe._accumulate_counts(8, fake, None, None) == 1
+    assert moe._load_imbalance(8, None, fake, None) == 1
+    assert moe._load_imbalance(8, fake, None, None) == 1
+    assert moe._score_bias_update(8, 0.1, None, fake, None, None) == 1
+    assert moe._score_bias_update(8, 0.1, fake, None, None, None) == 1
+    for g in (float("nan"), float("inf"), -float("inf")):
+        assert moe._score_bias_update(8, g, fake, fake, None, None) == 1
+        assert "bias_gamma" in moe._last_error().decode()

@@ -89,6 +89,9 @@ _experts_forward = _sig("moe_experts_forward", c_i32, _P(_CConfig), _P(_CWeights
 _combine = _sig("moe_combine", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp, c_vp)
 _latent_up = _sig("moe_latent_up", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp,
                   ctypes.c_size_t, c_vp)
+_accumulate_counts = _sig("moe_accumulate_expert_counts", c_i32, c_i32, c_vp, c_vp, c_vp)
+_load_imbalance = _sig("moe_load_imbalance", c_i32, c_i32, c_vp, c_vp, c_vp)
+_score_bias_update = _sig("moe_score_bias_update", c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp)
 
 
 class MoEError(RuntimeError):
@@ -384,3 +387,40 @@ def latent_up(cfg, weights: dict, n: torch.Tensor) -> torch.Tensor:
     _check(_latent_up(ctypes.byref(c), ctypes.byref(cw), T, _ptr(n), _ptr(y), _ptr(ws), ws.numel(),
                       _stream()))
     return y
+
+
+# --------------------------------------------------------------------------- balancing state
+# Page "Как устроен Olmo-core 3: обучение больших MoE-моделей", section "Счётчики и
+# bias-корректировка": the per-expert count accumulator, the load-imbalance metric and the
+# aux-loss-free score_bias update.
+
+def accumulate_expert_counts(batch_size_per_expert: torch.Tensor, accumulator: torch.Tensor) -> torch.Tensor:
+    """accumulator (E) int64 += batch_size_per_expert (E) int32, in place."""
+    E = accumulator.shape[0]
+    _expect(accumulator, (E,), torch.int64, "accumulator")
+    _expect(batch_size_per_expert, (E,), torch.int32, "batch_size_per_expert")
+    _check(_accumulate_counts(E, _ptr(batch_size_per_expert), _ptr(accumulator), _stream()))
+    return accumulator
+
+
+def load_imbalance(counts: torch.Tensor) -> torch.Tensor:
+    """max(counts) / mean(counts) of an (E) int64 counter, as a 0-dim float64 tensor on the
+    counter's device (NaN with no tokens)."""
+    E = counts.shape[0]
+    _expect(counts, (E,), torch.int64, "counts")
+    out = torch.empty((), dtype=torch.float64, device=counts.device)
+    _check(_load_imbalance(E, _ptr(counts), _ptr(out), _stream()))
+    return out
+
+
+def score_bias_update(accumulator: torch.Tensor, score_bias: torch.Tensor, bias_gamma: float,
+                      imbalance: bool = False) -> Optional[torch.Tensor]:
+    """score_bias (E) fp32 += bias_gamma * sign(total / E - accumulator), in place; zeroes the
+    accumulator. With imbalance=True returns the accumulator's load imbalance before the
+    reset (0-dim float64 tensor)."""
+    E = accumulator.shape[0]
+    _expect(accumulator, (E,), torch.int64, "accumulator")
+    _expect(score_bias, (E,), torch.float32, "score_bias")
+    out = torch.empty((), dtype=torch.float64, device=accumulator.device) if imbalance else None
+    _check(_score_bias_update(E, float(bias_gamma), _ptr(accumulator), _ptr(score_bias), _ptr(out), _stream()))
+    return out

@@ -579,3 +579,47 @@ moe_status_t moe_latent_up(const moe_config_t* c, const moe_weights_t* w, int64_
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------ balancing state
+
+namespace {
+moe_status_t check_experts(int32_t E) {
+  if (E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts must be in 1.." + std::to_string(MOE_MAX_EXPERTS));
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_accumulate_expert_counts(int32_t E, const int32_t* counts, int64_t* acc, void* stream) {
+  moe_status_t st;
+  if ((st = check_experts(E)) != MOE_OK) return st;
+  if ((st = need(counts, "batch_size_per_expert")) != MOE_OK) return st;
+  if ((st = need(acc, "accumulator")) != MOE_OK) return st;
+  MOE_TRY_HIP(launch_accumulate_counts(E, counts, acc, static_cast<hipStream_t>(stream)), "accumulate counts");
+  return ok();
+}
+
+moe_status_t moe_load_imbalance(int32_t E, const int64_t* counts, double* imbalance, void* stream) {
+  moe_status_t st;
+  if ((st = check_experts(E)) != MOE_OK) return st;
+  if ((st = need(counts, "counts")) != MOE_OK) return st;
+  if ((st = need(imbalance, "imbalance")) != MOE_OK) return st;
+  MOE_TRY_HIP(launch_load_imbalance(E, counts, imbalance, static_cast<hipStream_t>(stream)), "load imbalance");
+  return ok();
+}
+
+moe_status_t moe_score_bias_update(int32_t E, float gamma, int64_t* acc, float* score_bias, double* imbalance,
+                                   void* stream) {
+  moe_status_t st;
+  if ((st = check_experts(E)) != MOE_OK) return st;
+  if (!finite(gamma)) return fail(MOE_ERR_INVALID_ARG, "bias_gamma must be finite");
+  if ((st = need(acc, "accumulator")) != MOE_OK) return st;
+  if ((st = need(score_bias, "score_bias")) != MOE_OK) return st;
+  MOE_TRY_HIP(launch_score_bias_update(E, gamma, acc, score_bias, imbalance, static_cast<hipStream_t>(stream)),
+              "score_bias update");
+  return ok();
+}
+
+}  // extern "C"

@@ -214,6 +214,15 @@ constexpr int kF32TileM = 64;
 hipError_t launch_gemm_f32(const GemmCall& c, bool a_is_bf16, const float* col_bias,
                            hipStream_t s);
 
+// Load-balancing state (E <= 1024): acc (E) int64 += counts (E) int32; the load imbalance
+// max * E / total of counts (E) int64 as fp64 (NaN with no tokens); the score_bias update by
+// gamma * sign(total - E * acc[e]), which also zeroes acc and, when `imbalance` is not NULL,
+// writes the imbalance of acc before the reset.
+hipError_t launch_accumulate_counts(int E, const int32_t* counts, int64_t* acc, hipStream_t s);
+hipError_t launch_load_imbalance(int E, const int64_t* counts, double* out, hipStream_t s);
+hipError_t launch_score_bias_update(int E, float gamma, int64_t* acc, float* bias, double* imbalance,
+                                    hipStream_t s);
+
 // Weighted combine (+ RMSNorm): out (T, K) D.
 hipError_t launch_combine(const Layer& ly, const void* y_assign, const float* w,
                           const float* norm_weight, bool apply_norm, void* out, hipStream_t s);
