@@ -31,6 +31,10 @@ Readings where the pages are silent (each is listed with its reason in the desig
   * latent restore order: combine, then RMSNorm(eps, weight g, no bias), cast, up-projection;
   * down/up projections carry no bias; all weights are stored (out_features, in_features).
 
+Capacity ([OC3 "Ёмкость эксперта и переполнение"]): with a capacity_factor each expert keeps
+the first `capacity` assignments of the stable order and drops the rest (their expert output
+is 0), capacity = 8 * ceil(capacity_factor * top_k * T / (8 * E)).
+
 Balancing state ([OC3 "Счётчики и bias-корректировка"]): the count accumulator, the load
 imbalance metric max/mean, and the score_bias update by bias_gamma * sign(ideal - actual).
 
@@ -42,7 +46,9 @@ histogram/permutation against invariants and a brute-force counting sort; the ex
 against a dense evaluation of every expert on every token; special cases against torch's
 silu / rms_norm; permutation equivariance and RMSNorm scale invariance; the balancing
 state against closed forms (uniform load, one hot expert, fractional ideal) and against
-exact rational arithmetic (fractions.Fraction) on random counts.
+exact rational arithmetic (fractions.Fraction) on random counts; the capacity against
+hand-worked values, a first-come-first-kept walk over the assignments and a dense evaluation
+with the kept mask.
 """
 from __future__ import annotations
 
@@ -77,6 +83,7 @@ class MoEConfig:
     up_proj_input_norm: bool = True
     up_proj_input_norm_eps: float = 1e-5
     dtype: str = "bf16"
+    capacity_factor: Optional[float] = None
 
     @classmethod
     def from_dict(cls, d: dict) -> "MoEConfig":
@@ -262,6 +269,47 @@ def stable_permutation(idx):
     return perm, inv
 
 
+def expert_capacity(cfg: MoEConfig, num_tokens: int) -> Optional[int]:
+    """[OC3 "Ёмкость эксперта и переполнение"]: expert capacity = (expert-parallel degree) x
+    (allowed local inputs per expert); the allowed number is capacity_factor x the ideal
+    number of inputs, rounded up to a multiple of eight; the ideal number is top_k x
+    local_batch_size / num_experts. One process: degree 1, local batch = the num_tokens
+    tokens. Exact rational arithmetic on the fp32 capacity_factor. None = no capacity
+    (dropless)."""
+    if not cfg.capacity_factor:
+        return None
+    from fractions import Fraction
+    import math
+    allowed = Fraction(float(np.float32(cfg.capacity_factor))) * Fraction(cfg.top_k * num_tokens, cfg.num_experts)
+    return 8 * math.ceil(allowed / 8)
+
+
+def capacity_permutation(idx, num_experts: int, capacity: Optional[int]):
+    """[OC3 "Ёмкость эксперта и переполнение"]: on overflow every expert gets exactly
+    `capacity` inputs, the limit being applied when the local permutation gathers the tokens.
+    Read as: in the stable order of [OC3 "Пересылка токенов между экспертами"] (assignments
+    t*k+j sorted by expert, token order inside an expert) the first `capacity` assignments of
+    each expert are kept and the rest are dropped; a dropped assignment's expert output is 0.
+    Returns (perm, inv, kept): perm lists the kept assignments in that stable order, then the
+    dropped ones in the same order (so it stays a bijection of the A assignments); inv is its
+    inverse; kept (A,) bool. capacity None keeps everything (the plain stable permutation)."""
+    flat = np.asarray(idx).ravel()
+    order = np.argsort(flat, kind="stable").astype(np.int64)
+    if capacity is None:
+        kept = np.ones(flat.size, dtype=bool)
+        perm = order
+    else:
+        counts = np.bincount(flat, minlength=num_experts)
+        first = np.concatenate([[0], np.cumsum(counts)])[:-1]
+        rank = np.empty(flat.size, dtype=np.int64)
+        rank[order] = np.arange(flat.size) - first[flat[order]]
+        kept = rank < capacity
+        perm = np.concatenate([order[kept[order]], order[~kept[order]]])
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(flat.size)
+    return perm, inv, kept
+
+
 # ---------------------------------------------------------------------- experts
 
 def prepare_routed_input(cfg: MoEConfig, x, down_proj=None) -> np.ndarray:
@@ -290,20 +338,24 @@ def expert_mlp(cfg: MoEConfig, z_rows, w1_e, w2_e) -> np.ndarray:
     return round_to(act @ _f64(w2_e).T, cfg.dtype)
 
 
-def run_experts(cfg: MoEConfig, z, idx, w1, w2) -> dict:
+def run_experts(cfg: MoEConfig, z, idx, w1, w2, capacity: Optional[int] = None) -> dict:
     """[OC3 "Вычисления экспертов и точность"]: group the permuted tokens by expert, run each
     expert's MLP, and return the results; Y is kept in sorted (permuted) order here.
-    w1/w2 may be arrays (E, ...) or mappings expert -> array (only touched experts needed)."""
+    w1/w2 may be arrays (E, ...) or mappings expert -> array (only touched experts needed).
+    With a capacity ([OC3 "Ёмкость эксперта и переполнение"]) only the kept assignments run;
+    the rows of dropped assignments (after the kept ones in perm) stay 0. counts are the
+    router's counts before any drop; offsets delimit the kept rows of each expert."""
     k = cfg.top_k
     counts = expert_counts(idx, cfg.num_experts)
-    offsets = expert_offsets(counts)
-    perm, inv = stable_permutation(idx)
+    kept_counts = counts if capacity is None else np.minimum(counts, capacity)
+    offsets = expert_offsets(kept_counts)
+    perm, inv, kept = capacity_permutation(idx, cfg.num_experts, capacity)
     z_perm = _f64(z)[perm // k]
     Y = np.zeros((perm.size, _f64(z).shape[1]))
-    for e in np.nonzero(counts)[0]:
+    for e in np.nonzero(kept_counts)[0]:
         rows = slice(offsets[e], offsets[e + 1])
         Y[rows] = expert_mlp(cfg, z_perm[rows], w1[e], w2[e])
-    return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, z_perm=z_perm, Y=Y)
+    return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, kept=kept, z_perm=z_perm, Y=Y)
 
 
 def combine(cfg: MoEConfig, Y, inv, w) -> np.ndarray:
@@ -349,7 +401,8 @@ def forward(cfg: MoEConfig, weights: dict, x) -> dict:
     out.update(route(cfg, logits, weights.get("score_bias")))
     z = prepare_routed_input(cfg, x, weights.get("down_proj"))
     out["z"] = z
-    out.update(run_experts(cfg, z, out["idx"], weights["w1"], weights["w2"]))
+    out["capacity"] = expert_capacity(cfg, np.asarray(x).shape[0])
+    out.update(run_experts(cfg, z, out["idx"], weights["w1"], weights["w2"], out["capacity"]))
     o = combine(cfg, out["Y"], out["inv"], out["w"])
     out["o"] = o
     out.update(restore_routed_output(cfg, o, weights.get("norm_weight"), weights.get("up_proj")))

@@ -120,3 +120,42 @@ def test_planted_balance_mistake_is_caught(monkeypatch, target, bad, pin):
     monkeypatch.setattr(O, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+def _capacity_keeps_last(idx, num_experts, capacity):
+    flat = np.asarray(idx).ravel()
+    order = np.argsort(flat, kind="stable")
+    if capacity is None:
+        kept = np.ones(flat.size, dtype=bool)
+    else:
+        counts = np.bincount(flat, minlength=num_experts)
+        last = np.cumsum(counts)
+        rank_from_end = np.empty(flat.size, dtype=np.int64)
+        rank_from_end[order] = last[flat[order]] - 1 - np.arange(flat.size)
+        kept = rank_from_end < capacity  # keeps the last arrivals instead of the first
+    perm = np.concatenate([order[kept[order]], order[~kept[order]]])
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(flat.size)
+    return perm, inv, kept
+
+
+def _capacity_rounded_down(cfg, num_tokens):
+    if not cfg.capacity_factor:
+        return None
+    return 8 * int(cfg.capacity_factor * cfg.top_k * num_tokens / cfg.num_experts // 8)
+
+
+CAPACITY_MUTATIONS = [
+    ("capacity_permutation", _capacity_keeps_last,
+     lambda: P.test_capacity_permutation_against_first_come_walk(16, 4, 100, 16)),
+    ("expert_capacity", _capacity_rounded_down,
+     lambda: P.test_expert_capacity_hand_worked(1.25, 2, 100, 8, 32)),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", CAPACITY_MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in CAPACITY_MUTATIONS])
+def test_planted_capacity_mistake_is_caught(monkeypatch, target, bad, pin):
+    monkeypatch.setattr(O, target, bad)
+    with pytest.raises(AssertionError):
+        pin()

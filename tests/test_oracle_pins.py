@@ -6,6 +6,7 @@ tests/golden/), a library routine (torch's softmax / sigmoid / silu / rms_norm /
 Python's sort, math.fsum), brute force over all subsets, or an invariant of the method.
 CPU only.
 """
+import dataclasses
 import itertools
 import json
 import math
@@ -441,3 +442,93 @@ def test_accumulated_counts_equal_counts_of_all_batches():
         acc = O.accumulate_counts(acc, O.expert_counts(idx, E))
     every = np.concatenate([b.ravel() for b in batches])
     assert np.array_equal(acc, np.array([np.sum(every == e) for e in range(E)]))
+
+
+# ----------------------------------------------------------------- expert capacity
+# [OC3 "Ёмкость эксперта и переполнение"]: capacity = roundup8(capacity_factor * top_k * T / E)
+# at expert-parallel degree 1; each expert keeps the first `capacity` assignments of the
+# stable order; dropped assignments contribute nothing.
+
+CAPACITY_GOLDEN = [
+    # (capacity_factor, top_k, T, E, capacity) -- worked by hand
+    (1.0, 8, 8192, 64, 1024),     # ideal 1024, already a multiple of 8
+    (1.25, 2, 100, 8, 32),        # ideal 25, x1.25 = 31.25 -> 32
+    (1.0, 1, 1, 1024, 8),         # ideal 1/1024 -> rounds up to 8
+    (2.0, 8, 32768, 256, 2048),   # ideal 1024, x2
+    (0.5, 8, 16384, 896, 80),     # ideal 146.28..., x0.5 = 73.14... -> 80
+    (1.5, 4, 96, 32, 24),         # ideal 12, x1.5 = 18 -> 24
+    (1.0, 2, 12, 3, 8),           # ideal 8 exactly: stays 8
+]
+
+
+@pytest.mark.parametrize("cf,k,T,E,want", CAPACITY_GOLDEN)
+def test_expert_capacity_hand_worked(cf, k, T, E, want):
+    cfg = O.MoEConfig(d_model=64, num_experts=E, top_k=k, capacity_factor=cf)
+    assert O.expert_capacity(cfg, T) == want
+    assert O.expert_capacity(O.MoEConfig(d_model=64, num_experts=E, top_k=k), T) is None
+
+
+def _first_come_kept(idx, E, C):
+    """Walk the assignments in order t*k+j; an expert accepts until it holds C."""
+    held = [0] * E
+    kept = []
+    for e in np.asarray(idx).ravel():
+        kept.append(held[e] < C)
+        held[e] += 1
+    return np.array(kept)
+
+
+@pytest.mark.parametrize("E,k,T,C", [(4, 2, 37, 8), (16, 4, 100, 16), (7, 7, 9, 8), (32, 8, 300, 40),
+                                     (5, 1, 50, 8)])
+def test_capacity_permutation_against_first_come_walk(E, k, T, C):
+    rng = np.random.default_rng(E * 1000 + T)
+    # skewed choices so that some experts overflow
+    p = 1.0 / (np.arange(E) + 1.0)
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    perm, inv, kept = O.capacity_permutation(idx, E, C)
+    want_kept = _first_come_kept(idx, E, C)
+    assert np.array_equal(kept, want_kept)
+    flat = idx.ravel()
+    nk = int(want_kept.sum())
+    # kept assignments first, grouped by expert in token order; then the dropped ones alike
+    want_perm = sorted(range(flat.size), key=lambda a: (not want_kept[a], flat[a], a))
+    assert perm.tolist() == want_perm
+    assert np.array_equal(inv[perm], np.arange(flat.size))
+    counts = np.bincount(flat, minlength=E)
+    assert nk == int(np.minimum(counts, C).sum())
+    assert np.all(np.bincount(flat[perm[:nk]], minlength=E) == np.minimum(counts, C))
+
+
+def test_large_capacity_is_dropless():
+    cfg, w, x = small_workload("olmoe", 41, d_model=64, num_experts=7, top_k=3, hidden_size=64)
+    base = O.forward(cfg, w, x)
+    big = O.forward(dataclasses.replace(cfg, capacity_factor=1000.0), w, x)
+    assert big["capacity"] >= base["counts"].max()
+    assert np.array_equal(big["perm"], base["perm"]) and np.all(big["kept"])
+    assert np.array_equal(big["y"], base["y"])
+
+
+@pytest.mark.parametrize("name,over,rtol", [
+    ("tiny_f32", dict(d_model=64, num_experts=6, top_k=3, hidden_size=32, capacity_factor=0.5), 1e-6),
+    ("latent896", dict(d_model=128, latent_dim=64, num_experts=9, top_k=4, hidden_size=32,
+                       capacity_factor=0.75), 2e-2),
+])
+def test_capacity_dense_bruteforce(name, over, rtol):
+    """Every expert on every token, weighted by w and by the first-come kept mask, equals the
+    oracle's capacity path (sort, drop, group, zero the dropped rows, combine)."""
+    T = 53
+    cfg, w, x = small_workload(name, T, **over)
+    out = O.forward(cfg, w, x)
+    C = out["capacity"]
+    kept = _first_come_kept(out["idx"], cfg.num_experts, C).reshape(T, cfg.top_k)
+    assert not kept.all(), "the case must drop something"
+    rnd = _torch_round(cfg.dtype)
+    z = out["z"]
+    every = np.stack([_torch_swiglu_mlp(z, w["w1"][e], w["w2"][e], cfg.hidden_size, rnd).numpy()
+                      for e in range(cfg.num_experts)])
+    o = np.zeros((T, z.shape[1]))
+    for t in range(T):
+        for j in range(cfg.top_k):
+            if kept[t, j]:
+                o[t] += out["w"][t, j] * every[out["idx"][t, j], t]
+    assert np.abs(o - out["o"]).max() <= rtol * np.abs(o).max()
