@@ -95,6 +95,12 @@ typedef struct moe_config_t {
   int64_t latent_dim;                 /* L; 0 = no latent projection                           */
   int32_t up_proj_input_norm;         /* with latent: nonzero = bias-free RMSNorm before up-proj */
   float up_proj_input_norm_eps;       /* RMSNorm epsilon (page gives none; default 1e-5)       */
+  float capacity_factor;              /* > 0: expert capacity with token dropping
+                                         ([OC3 "Ёмкость эксперта и переполнение"]); 0 = dropless.
+                                         capacity = 8 * ceil(capacity_factor * top_k * T / (8 * E))
+                                         (expert-parallel degree 1, exact arithmetic); each expert
+                                         keeps the first `capacity` assignments of the stable
+                                         order, a dropped assignment's expert output is 0      */
 } moe_config_t;
 
 /*
@@ -121,10 +127,14 @@ typedef struct moe_weights_t {
 typedef struct moe_routing_t {
   float* expert_weights;           /* (T, k) fp32 combine weights, j in key-descending order   */
   int32_t* expert_indices;         /* (T, k) int32 selected experts, key-descending, ties low  */
-  int32_t* batch_size_per_expert;  /* (E) int32 token counts per expert
-                                      ([OC3 "Балансировка нагрузки и вспомогательные штрафы"])  */
-  int32_t* expert_offsets;         /* (E+1) int32 exclusive cumsum of the counts               */
-  int32_t* permutation;            /* (A) int32: sorted position p -> assignment t*k+j         */
+  int32_t* batch_size_per_expert;  /* (E) int32 token counts per expert, before any capacity
+                                      drop ([OC3 "Балансировка нагрузки и вспомогательные
+                                      штрафы"])                                                */
+  int32_t* expert_offsets;         /* (E+1) int32 exclusive cumsum of the counts; with a
+                                      capacity, of the kept counts min(count, capacity)        */
+  int32_t* permutation;            /* (A) int32: sorted position p -> assignment t*k+j; with a
+                                      capacity, positions >= expert_offsets[E] hold the dropped
+                                      assignments (same stable order)                          */
   int32_t* inverse_permutation;    /* (A) int32: assignment t*k+j -> sorted position p          */
   float* router_logits;            /* (T, E) fp32 logits                                       */
   float* router_scores;            /* (T, E) fp32 gating scores (softmax or sigmoid+eps)       */
@@ -156,6 +166,12 @@ MOE_API moe_status_t moe_config_validate(const moe_config_t* cfg);
  * 3*latent_dim*h*E, active = total - 3*latent_dim*h*E + 3*latent_dim*h*top_k, where
  * latent_dim is d_model without a latent projection. Either output pointer may be NULL. */
 MOE_API moe_status_t moe_num_params(const moe_config_t* cfg, int64_t* total, int64_t* active);
+
+/* Expert capacity for T tokens ([OC3 "Ёмкость эксперта и переполнение"]): 8 * ceil(
+ * capacity_factor * top_k * T / (8 * num_experts)) in exact arithmetic, at expert-parallel
+ * degree 1; values of T or more drop nothing and are reported as T rounded up to 8; 0 when
+ * capacity_factor is 0 (dropless). No GPU work. */
+MOE_API moe_status_t moe_expert_capacity(const moe_config_t* cfg, int64_t num_tokens, int64_t* capacity);
 
 /* Bytes of device workspace moe_forward needs for T tokens (also enough for every stage call
  * with the same cfg and T). T*k must stay below 2^31 (int32 offsets,
@@ -209,8 +225,11 @@ MOE_API moe_status_t moe_route_from_scores(const moe_config_t* cfg, int64_t num_
  * distinct within a row (not checked on the device; out-of-range entries are not counted and
  * get no position). Outputs (all required): batch_size_per_expert (E), expert_offsets (E+1),
  * permutation (A), inverse_permutation (A); the permutation is the stable sort of t*k+j by
- * expert. Uses the workspace. With T = 0 only the counts and offsets are written (zeros) and
- * the other pointers may be NULL.
+ * expert. With cfg.capacity_factor > 0 ([OC3 "Ёмкость эксперта и переполнение"]) each expert
+ * keeps the first `capacity` assignments of that order: the offsets delimit the kept rows, the
+ * permutation lists the kept assignments first and the dropped ones after them, and the counts
+ * stay the full histogram. Uses the workspace. With T = 0 only the counts and offsets are
+ * written (zeros) and the other pointers may be NULL.
  */
 MOE_API moe_status_t moe_permute(const moe_config_t* cfg, int64_t num_tokens,
                          const int32_t* expert_indices, int32_t* batch_size_per_expert,
@@ -236,7 +255,8 @@ MOE_API moe_status_t moe_latent_down(const moe_config_t* cfg, const moe_weights_
  * sigmoid(gate) (fp32, stored as D), Y = act * w2[e]^T in fp32 accumulation, rounded to D
  * (bf16 for bf16 layers: the grouped experts return bf16), and write Y to row
  * permutation[p] of y_assign (A, K) D -- i.e. y_assign is in assignment order t*k+j. Experts
- * with no rows read no weights. Uses the workspace.
+ * with no rows read no weights. With cfg.capacity_factor > 0 the rows p >= offsets[E] of the
+ * permutation are dropped assignments: their y_assign rows are set to 0. Uses the workspace.
  */
 MOE_API moe_status_t moe_experts_forward(const moe_config_t* cfg, const moe_weights_t* weights,
                                  int64_t num_tokens, const void* z, const int32_t* expert_offsets,

@@ -124,8 +124,10 @@ def routing_matches(cfgO: O.MoEConfig, gpu_idx, ref: dict, key_tol: float):
     return same
 
 
-def check_routing_invariants(cfg: dict, r: dict, T: int):
-    """Properties of the routing outputs that hold at any size (checked on the device)."""
+def check_routing_invariants(cfg: dict, r: dict, T: int, capacity=None):
+    """Properties of the routing outputs that hold at any size (checked on the device). With a
+    capacity, the offsets are those of the kept counts min(count, capacity) and the permutation
+    holds the kept assignments, then the dropped ones, each part sorted by expert and stable."""
     E, k = cfg["num_experts"], cfg["top_k"]
     idx = r["expert_indices"].long()
     assert idx.shape == (T, k)
@@ -134,8 +136,9 @@ def check_routing_invariants(cfg: dict, r: dict, T: int):
     assert bool((s[:, 1:] != s[:, :-1]).all()), "repeated expert within a token"
     counts = torch.bincount(idx.flatten(), minlength=E)
     assert torch.equal(counts.to(torch.int32), r["batch_size_per_expert"])
+    kept = counts if capacity is None else torch.clamp(counts, max=capacity)
     off = torch.zeros(E + 1, dtype=torch.int64, device=idx.device)
-    off[1:] = torch.cumsum(counts, 0)
+    off[1:] = torch.cumsum(kept, 0)
     assert torch.equal(off.to(torch.int32), r["expert_offsets"])
     perm = r["permutation"].long()
     inv = r["inverse_permutation"].long()
@@ -143,11 +146,15 @@ def check_routing_invariants(cfg: dict, r: dict, T: int):
     flat = idx.flatten()
     assert torch.equal(torch.sort(perm).values, torch.arange(A, device=perm.device))
     assert torch.equal(inv[perm], torch.arange(A, device=perm.device))
-    # sorted by expert, stable (assignment index increasing within an expert)
-    ep = flat[perm]
-    assert bool((ep[1:] >= ep[:-1]).all())
-    same_e = ep[1:] == ep[:-1]
-    assert bool((perm[1:][same_e] > perm[:-1][same_e]).all())
+    # each part sorted by expert, stable (assignment index increasing within an expert)
+    nk = int(off[E])
+    for part in (perm[:nk], perm[nk:]):
+        if part.numel() < 2:
+            continue
+        ep = flat[part]
+        assert bool((ep[1:] >= ep[:-1]).all())
+        same_e = ep[1:] == ep[:-1]
+        assert bool((part[1:][same_e] > part[:-1][same_e]).all())
 
 
 def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:

@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
                  "moe_config_default", "moe_config_validate", "moe_num_params",
                  "moe_workspace_size", "moe_status_string", "moe_last_error_message",
                  "moe_abi_version", "moe_accumulate_expert_counts", "moe_load_imbalance",
-                 "moe_score_bias_update"):
+                 "moe_score_bias_update", "moe_expert_capacity"):
         assert name in syms
 
 
@@ -162,3 +162,28 @@ def test_balancing_entry_points_validate_before_any_gpu_call():
     for g in (float("nan"), float("inf"), -float("inf")):
         assert moe._score_bias_update(8, g, fake, fake, None, None) == 1
         assert "bias_gamma" in moe._last_error().decode()
+
+
+CAPACITY_HOST_CASES = [(cf, k, T, E) for cf in (0.25, 0.5, 0.75, 1.0, 1.1, 1.25, 1.5, 2.0, 3.3, 1e-6, 7.0)
+                       for (k, T, E) in ((8, 8192, 64), (2, 100, 8), (1, 1, 1024), (8, 16384, 896),
+                                         (4, 97, 32), (16, 12345, 1000), (1, 5, 1))]
+
+
+@pytest.mark.parametrize("cf,k,T,E", CAPACITY_HOST_CASES)
+def test_expert_capacity_host_matches_oracle(cf, k, T, E):
+    """The library's host-side capacity (exact integer arithmetic) equals the oracle's exact
+    rational one; capacities of T or more drop nothing and are reported as T rounded up to 8."""
+    cfg = dict(d_model=64, num_experts=E, top_k=min(k, E), hidden_size=64, capacity_factor=cf)
+    want = O.expert_capacity(O.MoEConfig.from_dict(cfg), T)
+    got = moe.expert_capacity(cfg, T)
+    if want >= T:
+        assert got == (T + 7) // 8 * 8
+    else:
+        assert got == want
+    assert moe.expert_capacity(dict(cfg, capacity_factor=None), T) == 0
+
+
+def test_capacity_factor_validation():
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(moe.MoEError):
+            moe.validate(dict(d_model=64, num_experts=4, top_k=2, hidden_size=64, capacity_factor=bad))

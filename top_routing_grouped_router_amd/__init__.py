@@ -42,7 +42,7 @@ class _CConfig(ctypes.Structure):
         ("normalize_expert_weights", c_f32), ("restore_weight_scale", c_i32),
         ("expert_weight_scale", c_f32), ("original_top_k", c_i32), ("router_bias", c_i32),
         ("hidden_size", c_i64), ("activation", c_i32), ("dtype", c_i32), ("latent_dim", c_i64),
-        ("up_proj_input_norm", c_i32), ("up_proj_input_norm_eps", c_f32),
+        ("up_proj_input_norm", c_i32), ("up_proj_input_norm_eps", c_f32), ("capacity_factor", c_f32),
     ]
 
 
@@ -74,6 +74,7 @@ _config_default = _sig("moe_config_default", c_i32, _P(_CConfig))
 _config_validate = _sig("moe_config_validate", c_i32, _P(_CConfig))
 _num_params = _sig("moe_num_params", c_i32, _P(_CConfig), _P(c_i64), _P(c_i64))
 _workspace_size = _sig("moe_workspace_size", c_i32, _P(_CConfig), c_i64, _P(ctypes.c_size_t))
+_expert_capacity = _sig("moe_expert_capacity", c_i32, _P(_CConfig), c_i64, _P(c_i64))
 _forward = _sig("moe_forward", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp,
                 _P(_CRouting), c_vp, ctypes.c_size_t, c_vp)
 _router_forward = _sig("moe_router_forward", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp,
@@ -127,6 +128,7 @@ class MoEConfig:
     up_proj_input_norm: bool = True
     up_proj_input_norm_eps: float = 1e-5
     dtype: str = "bf16"
+    capacity_factor: Optional[float] = None
 
     @classmethod
     def of(cls, cfg) -> "MoEConfig":
@@ -153,6 +155,7 @@ class MoEConfig:
         c.up_proj_input_norm = int(bool(self.up_proj_input_norm))
         c.up_proj_input_norm_eps = float(self.up_proj_input_norm_eps)
         c.dtype = DTYPE[self.dtype]
+        c.capacity_factor = float(self.capacity_factor or 0.0)
         return c
 
     @property
@@ -174,6 +177,14 @@ def num_params(cfg) -> tuple[int, int]:
     total, active = c_i64(), c_i64()
     _check(_num_params(ctypes.byref(c), ctypes.byref(total), ctypes.byref(active)))
     return int(total.value), int(active.value)
+
+
+def expert_capacity(cfg, num_tokens: int) -> int:
+    """Expert capacity for num_tokens tokens (0 = dropless)."""
+    c = MoEConfig.of(cfg).to_c()
+    n = c_i64()
+    _check(_expert_capacity(ctypes.byref(c), int(num_tokens), ctypes.byref(n)))
+    return int(n.value)
 
 
 def workspace_size(cfg, num_tokens: int) -> int:

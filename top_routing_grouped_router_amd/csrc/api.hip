@@ -58,6 +58,8 @@ moe_status_t validate_config(const moe_config_t* c) {
     return fail(MOE_ERR_INVALID_ARG, "unknown gating_function");
   if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (!finite(c->capacity_factor) || c->capacity_factor < 0.f)
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite and >= 0 (0 = dropless)");
   if (!finite(c->sigmoid_stability_epsilon) || c->sigmoid_stability_epsilon < 0.f)
     return fail(MOE_ERR_INVALID_ARG, "sigmoid_stability_epsilon must be finite and >= 0");
   if (!finite(c->normalize_expert_weights) || c->normalize_expert_weights < 0.f)
@@ -85,6 +87,32 @@ moe_status_t validate_config(const moe_config_t* c) {
   return ok();
 }
 
+// [OC3 "Ёмкость эксперта и переполнение"]: capacity = 8 * ceil(cf * top_k * T / (8 * E)) at
+// expert-parallel degree 1, in exact integer arithmetic: cf = M * 2^(ex - 24) with M its 24-bit
+// integer significand. A capacity of at least T drops nothing (no expert receives more than T
+// assignments), so larger values are clamped to T rounded up to 8. 0 = dropless.
+int64_t expert_capacity(float cf, int32_t k, int64_t T, int32_t E) {
+  if (!(cf > 0.f) || T <= 0) return 0;
+  const int64_t no_drop = (T + 7) / 8 * 8;
+  if (static_cast<double>(cf) * k * static_cast<double>(T) / E >= static_cast<double>(T) + 16.0) return no_drop;
+  int ex = 0;
+  const double frac = frexp(static_cast<double>(cf), &ex);  // cf = frac * 2^ex, frac in [0.5, 1)
+  const __int128 M = static_cast<__int128>(ldexp(frac, 24));  // exact: cf has 24 significant bits
+  __int128 num = M * k * T;                                  // < 2^59
+  __int128 den = static_cast<__int128>(8) * E;
+  const int sh = ex - 24;                                    // value = num * 2^sh / den
+  if (sh >= 0) {
+    num <<= sh;  // sh is small here: cf * k * T / E < T + 16 bounds it
+  } else if (-sh < 64) {
+    den <<= -sh;
+  } else {
+    return 8;  // cf * k * T / E < 2^-20: the quotient rounds up to one block of 8
+  }
+  const __int128 q = (num + den - 1) / den;
+  const int64_t cap = static_cast<int64_t>(q) * 8;
+  return cap < no_drop ? cap : no_drop;
+}
+
 Layer make_layer(const moe_config_t* c, int64_t T) {
   Layer ly{};
   ly.T = T;
@@ -104,6 +132,7 @@ Layer make_layer(const moe_config_t* c, int64_t T) {
   ly.router_bias = c->router_bias != 0;
   ly.up_norm = c->up_proj_input_norm != 0;
   ly.norm_eps = c->up_proj_input_norm_eps;
+  ly.capacity = expert_capacity(c->capacity_factor, c->top_k, T, c->num_experts);
   return ly;
 }
 
@@ -360,6 +389,15 @@ moe_status_t moe_num_params(const moe_config_t* c, int64_t* total, int64_t* acti
   return ok();
 }
 
+moe_status_t moe_expert_capacity(const moe_config_t* c, int64_t T, int64_t* capacity) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if (!capacity) return fail(MOE_ERR_INVALID_ARG, "capacity is NULL");
+  *capacity = make_layer(c, T).capacity;
+  return ok();
+}
+
 moe_status_t moe_workspace_size(const moe_config_t* c, int64_t T, size_t* bytes) {
   moe_status_t st = validate_config(c);
   if (st != MOE_OK) return st;
@@ -413,6 +451,7 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
   }
   MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), at<void>(ws, L.yassign), s),
               "experts");
+  MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, at<void>(ws, L.yassign), s), "dropped rows");
   if (ly.L) {
     void* n = at<void>(ws, L.z);  // z is dead after the first expert GEMM
     MOE_TRY_HIP(launch_combine(ly, at<void>(ws, L.yassign), wts, w->up_proj_input_norm_weight, ly.up_norm, n, s),
@@ -537,6 +576,7 @@ moe_status_t moe_experts_forward(const moe_config_t* c, const moe_weights_t* w, 
   const TileList tiles = tiles_of(ws, L);
   MOE_TRY_HIP(launch_build_tiles(ly, offsets, tiles, expert_tile_m(ly), s), "tile list");
   MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), y_assign, s), "experts");
+  MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, y_assign, s), "dropped rows");
   return ok();
 }
 

@@ -122,6 +122,7 @@ struct Layer {
   bool router_bias;
   bool up_norm;
   float norm_eps;
+  int64_t capacity;  // expert capacity (token dropping); 0 = dropless
 };
 
 // Per-expert M-tile list consumed by the grouped GEMMs (device memory, built on the device).
@@ -163,6 +164,10 @@ size_t dispatch_scratch_bytes(const Layer& ly);
 hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
                            int bm, hipStream_t s);
+// With a capacity (ly.capacity > 0): zero the expert-output rows (assignment order, K wide) of
+// the dropped assignments, i.e. rows perm[p] for sorted positions p in [offsets[E], T*k).
+hipError_t launch_zero_dropped(const Layer& ly, const int32_t* offsets, const int32_t* perm, void* y,
+                               hipStream_t s);
 // Only the M-tile list, from existing offsets.
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
                               int bm, hipStream_t s);

@@ -25,6 +25,8 @@
 //   dispatch_small  all of the above in one workgroup for batches of at most 1024 tokens,
 //                   where four launches would cost more than the work.
 // Everything here moves O(T*k) int32 words: a few MB at the largest shapes.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -117,10 +119,13 @@ __global__ __launch_bounds__(256) void scan_cols_kernel(int32_t* __restrict__ bl
 }
 
 // counts -> offsets (or offsets given) -> M-tile list. One block of 1024 threads, E <= 1024.
+// With a capacity (> 0) the offsets are those of the kept counts min(count, capacity), and
+// drop_off (E + 1) receives the exclusive scan of the dropped counts.
 __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __restrict__ counts_in,
                                                              const int32_t* __restrict__ offsets_in,
                                                              int32_t* __restrict__ offsets_out,
-                                                             int E, int bm, TileList tiles) {
+                                                             int E, int bm, TileList tiles, int capacity,
+                                                             int32_t* __restrict__ drop_off) {
   __shared__ int sh[17];
   const int e = threadIdx.x;
   int c = 0, excl = 0;
@@ -130,11 +135,19 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
       c = offsets_in[e + 1] - excl;
     }
   } else {
-    c = e < E ? counts_in[e] : 0;
+    const int n = e < E ? counts_in[e] : 0;
+    c = capacity > 0 ? min(n, capacity) : n;
     excl = block_inclusive_scan(c, sh) - c;
     if (e < E) offsets_out[e] = excl;
     if (e == E - 1) offsets_out[E] = excl + c;
     __syncthreads();
+    if (capacity > 0) {
+      const int dc = n - c;
+      const int dexcl = block_inclusive_scan(dc, sh) - dc;
+      if (e < E) drop_off[e] = dexcl;
+      if (e == E - 1) drop_off[E] = dexcl + dc;
+      __syncthreads();
+    }
   }
   if (tiles.cap <= 0) return;
   c = c < 0 ? 0 : c;
@@ -152,12 +165,22 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
   if (threadIdx.x == 0) *tiles.count = min(total, tiles.cap);
 }
 
+// Position of an assignment whose rank inside its expert's stable order is r: the kept rows
+// (r < capacity, or no capacity) follow the expert offsets; the dropped ones come after all
+// kept rows, grouped by expert in the same order.
+__device__ __forceinline__ int64_t sorted_position(int64_t r, int e, int E, const int32_t* off,
+                                                   const int32_t* drop_off, int capacity) {
+  if (capacity <= 0 || r < capacity) return static_cast<int64_t>(off[e]) + r;
+  return static_cast<int64_t>(off[E]) + drop_off[e] + (r - capacity);
+}
+
 __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ rank,
                                                       const int32_t* __restrict__ blk, int nblk,
                                                       const int32_t* __restrict__ offsets, int64_t A,
                                                       int k, int E, int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ inv) {
+                                                      int32_t* __restrict__ inv, int capacity,
+                                                      const int32_t* __restrict__ drop_off) {
   const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (a >= A) return;
   const int e = idx[a];
@@ -167,9 +190,25 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   }
   const int64_t t = a / k;
   const int64_t b = t / kRankTokens;
-  const int64_t pos = static_cast<int64_t>(offsets[e]) + blk[static_cast<int64_t>(e) * nblk + b] + rank[a];
+  const int64_t r = static_cast<int64_t>(blk[static_cast<int64_t>(e) * nblk + b]) + rank[a];
+  const int64_t pos = sorted_position(r, e, E, offsets, drop_off, capacity);
   if (pos >= 0 && pos < A) perm[pos] = static_cast<int32_t>(a);
   inv[a] = static_cast<int32_t>(pos);
+}
+
+// Rows of the expert output (assignment order) of dropped assignments are zero: sorted
+// positions p in [offsets[E], A) hold them, row perm[p] of y (row_bytes each, a multiple of 16).
+__global__ __launch_bounds__(256) void zero_dropped_kernel(const int32_t* __restrict__ offsets, int E,
+                                                           const int32_t* __restrict__ perm, int64_t A,
+                                                           unsigned char* __restrict__ y, int64_t row_bytes) {
+  const int64_t p0 = min(max(static_cast<int64_t>(offsets[E]), int64_t(0)), A);
+  const int64_t cpr = row_bytes / 16;
+  const int64_t n = (A - p0) * cpr;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t a = perm[p0 + i / cpr];
+    if (a >= 0 && a < A) *reinterpret_cast<uint4*>(y + a * row_bytes + (i % cpr) * 16) = make_uint4(0, 0, 0, 0);
+  }
 }
 
 int num_rank_blocks(int64_t T) { return static_cast<int>((T + kRankTokens - 1) / kRankTokens); }
@@ -205,14 +244,18 @@ constexpr int kSmallTokens = 1024;
 __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ idx, int64_t T, int k,
                                                              int E, int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                             int32_t* __restrict__ inv, TileList tiles, int bm) {
+                                                             int32_t* __restrict__ inv, TileList tiles, int bm,
+                                                             int capacity) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* bits = reinterpret_cast<uint64_t*>(smem);  // [4][E]
   int32_t* pre = reinterpret_cast<int32_t*>(bits + 4 * E);  // [4][E]
   int32_t* run = pre + 4 * E;                           // [E] counts, then running rank base
-  int32_t* off = run + E;                               // [E + 1] offsets
-  int32_t* mt = pre;                                    // [E] M-tiles per expert (pass 1 only)
-  int32_t* tb = pre + E;                                // [E + 1] first tile of each expert (pass 1)
+  int32_t* off = run + E;                               // [E + 1] offsets (of the kept counts)
+  int32_t* doff = off + E + 1;                          // [E + 1] offsets of the dropped counts
+  int32_t* kc = pre;                                    // [E] kept counts (pass 1 only)
+  int32_t* dc = pre + E;                                // [E] dropped counts (pass 1 only)
+  int32_t* mt = pre + 2 * E;                            // [E] M-tiles per expert (pass 1 only)
+  int32_t* tb = pre;                                    // [E + 1] first tile of each expert (pass 1)
   __shared__ int sh[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t A = T * k;
@@ -224,12 +267,19 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     if (e >= 0 && e < E) atomicAdd(&run[e], 1);
   }
   __syncthreads();
-  block_exclusive_scan_e(run, E, off, sh);
+  for (int e = tid; e < E; e += 256) {
+    kc[e] = capacity > 0 ? min(run[e], capacity) : run[e];
+    dc[e] = run[e] - kc[e];
+  }
+  __syncthreads();
+  block_exclusive_scan_e(kc, E, off, sh);
+  __syncthreads();
+  block_exclusive_scan_e(dc, E, doff, sh);
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
     counts[e] = run[e];
     offsets[e] = off[e];
-    mt[e] = (run[e] + bm - 1) / bm;
+    mt[e] = (off[e + 1] - off[e] + bm - 1) / bm;
   }
   if (tid == 0) offsets[E] = off[E];
   __syncthreads();
@@ -237,7 +287,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     block_exclusive_scan_e(mt, E, tb, sh);
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
-      const int c = run[e];
+      const int c = off[e + 1] - off[e];
       for (int i = 0; i < mt[e]; ++i) {
         const int ti = tb[e] + i;
         if (ti >= tiles.cap) break;
@@ -282,7 +332,8 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
           inv[a] = -1;
           continue;
         }
-        const int64_t pos = static_cast<int64_t>(off[e]) + pre[wave * E + e] + __popcll(bits[wave * E + e] & below);
+        const int64_t r = static_cast<int64_t>(pre[wave * E + e]) + __popcll(bits[wave * E + e] & below);
+        const int64_t pos = sorted_position(r, e, E, off, doff, capacity);
         if (pos >= 0 && pos < A) perm[pos] = static_cast<int32_t>(a);
         inv[a] = static_cast<int32_t>(pos);
       }
@@ -296,40 +347,56 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
 size_t dispatch_scratch_bytes(const Layer& ly) {
   const size_t A = static_cast<size_t>(ly.T) * ly.k;
   const size_t nblk = static_cast<size_t>(num_rank_blocks(ly.T));
-  return (A + static_cast<size_t>(ly.E) * nblk) * sizeof(int32_t) + 256;
+  // rank (A), block counts (E, nblk), dropped-count offsets (E + 1)
+  return (A + static_cast<size_t>(ly.E) * nblk + static_cast<size_t>(ly.E) + 1) * sizeof(int32_t) + 256;
 }
 
 hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
                            int bm, hipStream_t s) {
   if (ly.T <= 0) return hipSuccess;
+  const int cap = static_cast<int>(ly.capacity);  // <= T rounded up to 8, below 2^31
   if (ly.T <= kSmallTokens) {
-    // bits [4][E] u64, pre [4][E], run [E], off [E + 1]: 56 E + 4 bytes (57 KiB at E = 1024)
+    // bits [4][E] u64, pre [4][E], run [E], off [E + 1], doff [E + 1]: 60 E + 8 bytes
+    // (61 KiB at E = 1024)
     const size_t lds = static_cast<size_t>(ly.E) * 4 * (sizeof(uint64_t) + sizeof(int32_t)) +
-                       static_cast<size_t>(2 * ly.E + 1) * sizeof(int32_t);
+                       static_cast<size_t>(3 * ly.E + 2) * sizeof(int32_t);
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), lds, s, idx, ly.T, ly.k, ly.E, counts, offsets,
-                       perm, inv, tiles, bm);
+                       perm, inv, tiles, bm, cap);
     return hipGetLastError();
   }
   const int nblk = num_rank_blocks(ly.T);
   const int64_t A = ly.T * ly.k;
   int32_t* rank = static_cast<int32_t*>(scratch);
   int32_t* blk = rank + A;
+  int32_t* drop_off = blk + static_cast<int64_t>(ly.E) * nblk;
   const size_t lds = static_cast<size_t>(ly.E) * 4 * (sizeof(uint64_t) + sizeof(int32_t));
   hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(256), lds, s, idx, ly.T, ly.k, ly.E, nblk, rank,
                      blk);
   hipLaunchKernelGGL(scan_cols_kernel, dim3(ly.E), dim3(256), 0, s, blk, nblk, counts);
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, counts, nullptr, offsets, ly.E,
-                     bm, tiles);
+                     bm, tiles, cap, drop_off);
   hipLaunchKernelGGL(permute_kernel, dim3(static_cast<unsigned>((A + 255) / 256)), dim3(256), 0, s,
-                     idx, rank, blk, nblk, offsets, A, ly.k, ly.E, perm, inv);
+                     idx, rank, blk, nblk, offsets, A, ly.k, ly.E, perm, inv, cap, drop_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_dropped(const Layer& ly, const int32_t* offsets, const int32_t* perm, void* y,
+                               hipStream_t s) {
+  const int64_t A = ly.T * ly.k;
+  if (ly.capacity <= 0 || A <= 0) return hipSuccess;
+  const int64_t row_bytes = ly.K * (ly.bf16 ? 2 : 4);
+  const int64_t chunks = A * (row_bytes / 16);
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((chunks + 255) / 256, 2048));
+  hipLaunchKernelGGL(zero_dropped_kernel, dim3(grid), dim3(256), 0, s, offsets, ly.E, perm, A,
+                     static_cast<unsigned char*>(y), row_bytes);
   return hipGetLastError();
 }
 
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
                               int bm, hipStream_t s) {
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, nullptr, offsets, nullptr,
-                     ly.E, bm, tiles);
+                     ly.E, bm, tiles, 0, nullptr);
   return hipGetLastError();
 }
 
