@@ -84,6 +84,7 @@ class MoEConfig:
     up_proj_input_norm_eps: float = 1e-5
     dtype: str = "bf16"
     capacity_factor: Optional[float] = None
+    expert_precision: str = "bf16"   # "bf16" or "mxfp8" (the expert matmuls)
 
     @classmethod
     def from_dict(cls, d: dict) -> "MoEConfig":
@@ -310,6 +311,98 @@ def capacity_permutation(idx, num_experts: int, capacity: Optional[int]):
     return perm, inv, kept
 
 
+# ------------------------------------------------------------------- MXFP8 (expert GEMMs)
+# [OC3 "Rowwise FP8 и MXFP8"] and [OC3 "Как сравнивали и что получилось"]: the grouped expert
+# matmuls can run in MXFP8 (the page measures it against BF16). The page does not spell the
+# format out; read as the OCP microscaling format: blocks of 32 consecutive elements along the
+# contraction dimension share one power-of-two scale (E8M0), elements are FP8 E4M3 (1 sign,
+# 4 exponent bits with bias 7, 3 mantissa bits, no infinities, max 448). Scale exponent =
+# floor(log2(amax of the block)) - 8 (8 = the largest E4M3 exponent), elements = the block /
+# 2^exponent rounded to nearest-even E4M3, saturating at +-448. An all-zero block gets the
+# smallest scale, 2^-127 (E8M0 code 0).
+
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """The 256 E4M3 codes as float64 (NaN for the two NaN codes 0x7F, 0xFF)."""
+    c = np.arange(256)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return sign * v
+
+
+def e4m3_encode(a) -> np.ndarray:
+    """Round-to-nearest-even E4M3 codes of float64 values, saturating at +-448 (NaN input ->
+    NaN code 0x7F). The sign of zero is kept."""
+    a = np.asarray(a, np.float64)
+    mag = np.minimum(np.abs(a), E4M3_MAX)
+    # exponent of the E4M3 binade (subnormals share the spacing of the smallest normal binade)
+    with np.errstate(divide="ignore"):
+        ex = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    ex = np.clip(ex, -6, 8)
+    step = 2.0 ** (ex - 3)                      # spacing of 3 mantissa bits in that binade
+    q = mag / step                              # exact: power-of-two division
+    r = np.floor(q)
+    frac = q - r
+    r = np.where((frac > 0.5) | ((frac == 0.5) & (r % 2 == 1)), r + 1, r)
+    val = r * step                              # the rounded magnitude, on the E4M3 grid
+    # back to a code: biased exponent and mantissa of val
+    with np.errstate(divide="ignore"):
+        vex = np.floor(np.log2(np.where(val > 0, val, 1.0)))
+    normal = val >= 2.0 ** -6
+    code = np.where(normal, ((vex + 7).astype(np.int64) << 3) | ((val / 2.0 ** vex - 1.0) * 8).astype(np.int64),
+                    (val / 2.0 ** -9).astype(np.int64))
+    code = np.where(val == 0, 0, code)
+    code = code | np.where(np.signbit(a), 0x80, 0)
+    return np.where(np.isnan(a), 0x7F, code).astype(np.uint8)
+
+
+def mx_quantize(v, block: int = MX_BLOCK):
+    """MX quantisation of v (..., K) along its last axis (K a multiple of `block`). Returns
+    (codes uint8 (..., K), scale codes uint8 (..., K/block)) with scale = 2^(code - 127)."""
+    v = np.asarray(v, np.float64)
+    *lead, K = v.shape
+    b = v.reshape(*lead, K // block, block)
+    amax = np.abs(b).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8.0
+    scode = np.where(amax > 0, np.clip(ex + 127.0, 0, 254), 0).astype(np.int64)
+    codes = e4m3_encode(b / (2.0 ** (scode - 127.0))[..., None])
+    return codes.reshape(*lead, K), scode.astype(np.uint8)
+
+
+def mx_dequantize(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """Values of MX-quantised data: e4m3(code) * 2^(scale - 127), float64."""
+    codes = np.asarray(codes)
+    *lead, K = codes.shape
+    vals = e4m3_values()[codes].reshape(*lead, K // block, block)
+    return (vals * (2.0 ** (np.asarray(scales, np.float64) - 127.0))[..., None]).reshape(*lead, K)
+
+
+def mx_round(v, block: int = MX_BLOCK) -> np.ndarray:
+    """v as it is after MX quantisation (quantise, then dequantise)."""
+    return mx_dequantize(*mx_quantize(v, block), block)
+
+
+def expert_mlp_mxfp8(cfg: "MoEConfig", z_rows, w1_e, w2_e) -> np.ndarray:
+    """One expert's SwiGLU MLP with both matmuls in MXFP8 ([OC3 "Rowwise FP8 и MXFP8"], [OC3
+    "SwiGLU с квантизацией"]: the SwiGLU step yields the activation and its quantised form).
+    The operands are MX-quantised along the contraction dimension (z rows and W1 rows along K,
+    the activation rows and W2 rows along h); the products and sums are exact (float64); the
+    activation is stored in the layer dtype before it is quantised; the output is bf16."""
+    h = cfg.hidden_size
+    H = mx_round(z_rows) @ mx_round(w1_e).T
+    up, gate = H[:, :h], H[:, h:]
+    with np.errstate(over="ignore"):
+        act = round_to(up * gate / (1.0 + np.exp(-gate)), cfg.dtype)
+    return round_to(mx_round(act) @ mx_round(w2_e).T, cfg.dtype)
+
+
 # ---------------------------------------------------------------------- experts
 
 def prepare_routed_input(cfg: MoEConfig, x, down_proj=None) -> np.ndarray:
@@ -352,9 +445,10 @@ def run_experts(cfg: MoEConfig, z, idx, w1, w2, capacity: Optional[int] = None) 
     perm, inv, kept = capacity_permutation(idx, cfg.num_experts, capacity)
     z_perm = _f64(z)[perm // k]
     Y = np.zeros((perm.size, _f64(z).shape[1]))
+    mlp = expert_mlp_mxfp8 if cfg.expert_precision == "mxfp8" else expert_mlp
     for e in np.nonzero(kept_counts)[0]:
         rows = slice(offsets[e], offsets[e + 1])
-        Y[rows] = expert_mlp(cfg, z_perm[rows], w1[e], w2[e])
+        Y[rows] = mlp(cfg, z_perm[rows], w1[e], w2[e])
     return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, kept=kept, z_perm=z_perm, Y=Y)
 
 

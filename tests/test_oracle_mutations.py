@@ -159,3 +159,37 @@ def test_planted_capacity_mistake_is_caught(monkeypatch, target, bad, pin):
     monkeypatch.setattr(O, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+_orig_encode = O.e4m3_encode
+
+
+def _mx_scale_off_by_one(v, block=O.MX_BLOCK):
+    v = np.asarray(v, np.float64)
+    *lead, K = v.shape
+    b = v.reshape(*lead, K // block, block)
+    amax = np.abs(b).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 7.0  # uses the mantissa-less max 2^7
+    scode = np.where(amax > 0, np.clip(ex + 127.0, 0, 254), 0).astype(np.int64)
+    codes = _orig_encode(b / (2.0 ** (scode - 127.0))[..., None])
+    return codes.reshape(*lead, K), scode.astype(np.uint8)
+
+
+def _e4m3_ties_away(a):
+    a = np.asarray(a, np.float64)
+    up = _orig_encode(np.nextafter(np.abs(a), np.inf)) & 0x7F  # nudging up turns ties into round-up
+    return (up | np.where(np.signbit(a), 0x80, 0)).astype(np.uint8)
+
+
+MX_MUTATIONS = [
+    ("mx_quantize", _mx_scale_off_by_one, lambda: P.test_mx_quantize_block_scale_definition(0)),
+    ("e4m3_encode", _e4m3_ties_away, lambda: P.test_e4m3_encode_matches_torch_float8()),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", MX_MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MX_MUTATIONS])
+def test_planted_mx_mistake_is_caught(monkeypatch, target, bad, pin):
+    monkeypatch.setattr(O, target, bad)
+    with pytest.raises(AssertionError):
+        pin()

@@ -532,3 +532,91 @@ def test_capacity_dense_bruteforce(name, over, rtol):
             if kept[t, j]:
                 o[t] += out["w"][t, j] * every[out["idx"][t, j], t]
     assert np.abs(o - out["o"]).max() <= rtol * np.abs(o).max()
+
+
+# ----------------------------------------------------------------- MXFP8
+# OCP microscaling read of [OC3 "Rowwise FP8 и MXFP8"]: E4M3 elements, E8M0 block scales,
+# blocks of 32 along the contraction dimension.
+
+def _e4m3_ties_and_edges():
+    grid = O.e4m3_values()[:0x7F]           # the 127 finite non-negative codes, increasing
+    mids = (grid[1:] + grid[:-1]) / 2.0     # exact midpoints: ties
+    vals = np.concatenate([grid, mids, np.nextafter(mids, 0.0), np.nextafter(mids, 1e9), [448.0, 0.0]])
+    vals = np.concatenate([vals, -vals])
+    return vals.astype(np.float32)
+
+
+def test_e4m3_encode_matches_torch_float8():
+    """torch's float8_e4m3fn cast (round to nearest even) on every grid point, every midpoint
+    (exact ties), the neighbours of every midpoint, and random values over the whole range."""
+    rng = np.random.default_rng(3)
+    rand = rng.standard_normal(50000) * np.exp(rng.uniform(-14, 6.1, 50000))
+    x = np.concatenate([_e4m3_ties_and_edges(), np.clip(rand, -448, 448).astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), want)
+    assert np.signbit(O.e4m3_values()[O.e4m3_encode(np.float32(-0.0))])  # -0 keeps its sign
+
+
+def test_e4m3_encode_brute_force_and_saturation():
+    grid = O.e4m3_values()[:0x7F]
+    rng = np.random.default_rng(4)
+    for a in np.abs(rng.standard_normal(3000) * 2.0 ** rng.uniform(-10, 8, 3000)):
+        d = np.abs(grid - min(a, 448.0))
+        best = np.nonzero(d == d.min())[0]
+        want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]  # ties: even mantissa
+        assert O.e4m3_encode(a) == want
+    assert list(O.e4m3_encode([448.0, 449.0, 1e30, -500.0])) == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mx_quantize_block_scale_definition(seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((7, 256)) * np.exp(rng.uniform(-8, 8, (7, 1)))
+    v[2, 64:96] = 0.0                                      # an all-zero block
+    codes, scales = O.mx_quantize(v)
+    b = v.reshape(7, 8, 32)
+    amax = np.abs(b).max(-1)
+    nz = amax > 0
+    ratio = amax[nz] / 2.0 ** (scales[nz].astype(np.float64) - 127)
+    assert np.all((ratio >= 256) & (ratio < 512))          # exponent = floor(log2 amax) - 8
+    assert scales[2, 2] == 0 and np.all(codes[2, 64:96] & 0x7F == 0)
+    deq = O.mx_dequantize(codes, scales).reshape(7, 8, 32)
+    step = 2.0 ** (scales.astype(np.float64) - 127)[..., None] * 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b) / 2.0 ** (scales.astype(np.float64) - 127)[..., None], 2.0 ** -6))) - 3)
+    sat = np.abs(b) / 2.0 ** (scales.astype(np.float64) - 127)[..., None] > 448
+    assert np.all(np.abs(deq - b)[~sat] <= step[~sat] / 2)  # nearest grid point
+    assert np.all(np.abs(deq[sat]) == 448 * 2.0 ** (scales.astype(np.float64) - 127)[..., None].repeat(32, -1)[sat])
+
+
+def test_mx_round_trip_of_representable_blocks():
+    rng = np.random.default_rng(5)
+    grid = O.e4m3_values()[:0x7F]
+    for e in (-20, -3, 0, 5, 30):
+        blk = rng.choice(grid, size=(4, 32)) * rng.choice([-1.0, 1.0], size=(4, 32))
+        blk[:, 0] = 256.0 * np.sign(blk[:, 0] + 0.5)       # amax in [256, 512): scale exactly 2^e
+        v = blk * 2.0 ** e
+        assert np.array_equal(O.mx_round(v), v)
+
+
+def test_mxfp8_dense_bruteforce_equals_permuted_path():
+    """The MXFP8 expert path through sort/group/combine equals every expert's MXFP8 MLP on
+    every token (torch's silu, operands rounded through MX independently of the permutation)."""
+    T = 37
+    cfg, w, x = small_workload("olmoe", T, d_model=128, num_experts=5, top_k=2, hidden_size=64,
+                               expert_precision="mxfp8")
+    out = O.forward(cfg, w, x)
+    z = out["z"]
+    every = []
+    for e in range(cfg.num_experts):
+        H = torch.from_numpy(O.mx_round(z)) @ torch.from_numpy(O.mx_round(w["w1"][e])).T
+        up, gate = H[:, :64], H[:, 64:]
+        act = _torch_round("bf16")(up * torch.nn.functional.silu(gate))
+        every.append(_torch_round("bf16")(torch.from_numpy(O.mx_round(act.numpy())) @
+                                          torch.from_numpy(O.mx_round(w["w2"][e])).T).numpy())
+    o = np.zeros_like(out["o"])
+    for t in range(T):
+        for j in range(cfg.top_k):
+            o[t] += out["w"][t, j] * every[out["idx"][t, j]][t]
+    assert np.abs(o - out["o"]).max() <= 1e-2 * np.abs(o).max()
+    # and the MXFP8 layer stays close to the bf16 one (quantisation error only)
+    ref = O.forward(dataclasses.replace(cfg, expert_precision="bf16"), w, x)
+    assert np.linalg.norm(out["y"] - ref["y"]) <= 0.1 * np.linalg.norm(ref["y"])

@@ -44,6 +44,7 @@ _LAYER_DEFAULTS = dict(
     up_proj_input_norm_eps=1e-5,
     dtype="bf16",
     capacity_factor=None,
+    expert_precision="bf16",
 )
 
 LAYER_FIELDS = tuple(_LAYER_DEFAULTS)
