@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (MXFP8 experts)
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -31,6 +32,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe")
+    ap.add_argument("--precision", default="bf16", choices=("bf16", "mxfp8"),
+                    help="precision of the expert matmuls (mxfp8: block-scaled E4M3 on the fp8 matrix cores)")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -200,13 +203,14 @@ def main():
     import workloads
 
     name = args.workload
-    cfg, w, x = workloads.make_workload(name, device="cuda")
+    cfg, w, x = workloads.make_workload(name, device="cuda", expert_precision=args.precision)
     T = x.shape[0]
     E, k, h = cfg["num_experts"], cfg["top_k"], cfg["hidden_size"]
     d, L = cfg["d_model"], cfg["latent_dim"] or 0
     K = L or d
     A = T * k
     layer = moe.MoELayer(cfg, w)
+    w = layer.weights  # with the MXFP8 weight copies when the experts run in MXFP8
     y = torch.empty_like(x)
 
     for _ in range(args.warmup):
@@ -228,6 +232,7 @@ def main():
     gemm_ms = event_time_ms(lambda: moe.experts_forward(cfg, w, z, offs, perm), max(args.steps, 5), torch)
     gemm_flops = 6.0 * A * K * h
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
+    peak = PEAK_FP8_TFLOPS if args.precision == "mxfp8" else PEAK_BF16_TFLOPS
     layer_flops = 2.0 * T * d * E + gemm_flops + (4.0 * T * d * L if L else 0.0)
 
     out = {
@@ -241,15 +246,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg["dtype"] == "bf16" else "f32",
+        "dtype": ("mxfp8 experts, bf16" if args.precision == "mxfp8" else "bf16") if cfg["dtype"] == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": name, "tokens": T, "d_model": d, "num_experts": E, "top_k": k,
                    "hidden_size": h, "latent_dim": L or None, "gating": cfg["gating_function"],
-                   "router": "fp32", "parallelism": "none (1 GPU)"},
+                   "router": "fp32", "expert_precision": args.precision, "parallelism": "none (1 GPU)"},
         "layer_tflops": round(layer_flops / (ms / 1e3) / 1e12, 2),
         "roofline": {"kernel": "grouped expert GEMMs (up/gate+SwiGLU, down)", "bound": "mfma",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(name),
+                     "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(name) if args.precision == "bf16" else None,
                      "stage_ms": round(gemm_ms, 4), "flops_per_launch": gemm_flops},
     }
     if args.stages:

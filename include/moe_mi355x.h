@@ -71,6 +71,14 @@ typedef enum { MOE_ACT_SWIGLU = 0 } moe_activation_t;
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 
+/* Precision of the grouped expert matmuls ([OC3 "Rowwise FP8 и MXFP8"], [OC3 "Как сравнивали
+ * и что получилось"]: the page compares MXFP8 against BF16). MXFP8 (see moe_mx_quantize):
+ * the expert inputs z and the SwiGLU activation are MX-quantised along the contraction
+ * dimension inside the experts stage, the weights come pre-quantised (moe_weights_t.w*_mx),
+ * products accumulate in fp32 on the block-scaled matrix cores, outputs are bf16 as before.
+ * Requires dtype bf16 and d_model / latent_dim and hidden_size multiples of 128. */
+typedef enum { MOE_PRECISION_BF16 = 0, MOE_PRECISION_MXFP8 = 1 } moe_precision_t;
+
 /*
  * Layer configuration. Field names follow MoEConfig / MoERouterConfigV2 / LatentMoEConfig
  * ([OC3 "Как задаётся конфигурация MoE"], [OC3 "Маршрутизация: как роутер выбирает
@@ -101,6 +109,7 @@ typedef struct moe_config_t {
                                          (expert-parallel degree 1, exact arithmetic); each expert
                                          keeps the first `capacity` assignments of the stable
                                          order, a dropped assignment's expert output is 0      */
+  int32_t expert_precision;           /* moe_precision_t of the expert matmuls (default BF16)  */
 } moe_config_t;
 
 /*
@@ -118,6 +127,13 @@ typedef struct moe_weights_t {
   const void* w1;              /* (E, 2h, K) D: rows [0, h) = up, rows [h, 2h) = gate
                                   ([OC3 "SwiGLU с квантизацией"] splits up then gate)           */
   const void* w2;              /* (E, K, h) D                                                  */
+  /* MXFP8 experts (cfg.expert_precision = MXFP8) read these instead of w1 / w2: the same
+   * matrices as E4M3 codes with E8M0 block scales from moe_mx_quantize (blocks of 32 along
+   * each row, i.e. along K for w1 and along h for w2).                                       */
+  const uint8_t* w1_mx;        /* (E, 2h, K) codes                                             */
+  const uint8_t* w1_mx_scale;  /* (E, 2h, K/32) scales                                         */
+  const uint8_t* w2_mx;        /* (E, K, h) codes                                              */
+  const uint8_t* w2_mx_scale;  /* (E, K, h/32) scales                                          */
 } moe_weights_t;
 
 /*
@@ -282,6 +298,22 @@ MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const moe_weights_t* w
 MOE_API moe_status_t moe_latent_up(const moe_config_t* cfg, const moe_weights_t* weights,
                            int64_t num_tokens, const void* n, void* y, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* ------------------------------------------------------------------------ MXFP8 */
+
+/*
+ * MXFP8 quantisation of bf16 rows ([OC3 "Rowwise FP8 и MXFP8"]; the page does not define the
+ * format, read as OCP microscaling): each block of 32 consecutive elements of a row shares one
+ * E8M0 scale byte s (value 2^(s - 127)) with s - 127 = floor(log2(amax of the block)) - 8,
+ * clamped to [-127, 127] (an all-zero block gets s = 0); the elements are FP8 E4M3 (OCP: bias
+ * 7, 3 mantissa bits, max 448) of value / 2^(s - 127), rounded to nearest-even and saturated
+ * at +-448. x (rows, cols) bf16 -> codes (rows, cols) uint8 and scales (rows, cols / 32) uint8,
+ * row-major. cols must be a positive multiple of 32 (INVALID_ARG otherwise); inputs must be
+ * finite. Used to pre-quantise the expert weights for cfg.expert_precision = MXFP8 (W1 rows
+ * along K, W2 rows along h).
+ */
+MOE_API moe_status_t moe_mx_quantize(int64_t rows, int64_t cols, const void* x, uint8_t* codes, uint8_t* scales,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------ balancing state */
 

@@ -163,3 +163,29 @@ def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
         return np.arange(T)
     s = set(g.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
     return np.array(sorted(s))
+
+
+# MXFP8 experts: the block-scaled matrix cores sum their products with an error up to about
+# 2^-12 of sum_k |a_k b_k| per instruction (measured on gfx950 against exact products), where
+# the oracle sums exactly. Allowance per expert-output element: 2^-10 * sum_k |act_q,k| |w2_q,k|
+# (the GEMM2 bound with a factor 4 of headroom, which also covers the rare activation codes that
+# GEMM1's error moves across an fp8 rounding boundary).
+MX_SUM_ERR = 2.0 ** -10
+
+
+def mx_expert_allowance(cfgO, ex, wo):
+    """Per-row allowance (A, K) in sorted order for an oracle run_experts result `ex`."""
+    from oracle import moe_oracle as O
+    h = cfgO.hidden_size
+    out = np.zeros_like(ex["Y"])
+    off = ex["offsets"]
+    for e in range(cfgO.num_experts):
+        rows = slice(off[e], off[e + 1])
+        if off[e + 1] == off[e]:
+            continue
+        H = O.mx_round(ex["z_perm"][rows]) @ O.mx_round(np.asarray(wo["w1"][e], np.float64)).T
+        up, gate = H[:, :h], H[:, h:]
+        with np.errstate(over="ignore"):
+            act = O.round_to(up * gate / (1.0 + np.exp(-gate)), cfgO.dtype)
+        out[rows] = MX_SUM_ERR * (np.abs(O.mx_round(act)) @ np.abs(O.mx_round(np.asarray(wo["w2"][e], np.float64))).T)
+    return out

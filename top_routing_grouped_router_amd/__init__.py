@@ -32,6 +32,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 GATING = {"softmax": 0, "topk_softmax": 1, "sigmoid": 2}
 DTYPE = {"f32": 0, "bf16": 1}
+PRECISION = {"bf16": 0, "mxfp8": 1}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -43,12 +44,14 @@ class _CConfig(ctypes.Structure):
         ("expert_weight_scale", c_f32), ("original_top_k", c_i32), ("router_bias", c_i32),
         ("hidden_size", c_i64), ("activation", c_i32), ("dtype", c_i32), ("latent_dim", c_i64),
         ("up_proj_input_norm", c_i32), ("up_proj_input_norm_eps", c_f32), ("capacity_factor", c_f32),
+        ("expert_precision", c_i32),
     ]
 
 
 class _CWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ("router_weight", "router_bias", "score_bias", "down_proj",
-                                    "up_proj_input_norm_weight", "up_proj", "w1", "w2")]
+                                    "up_proj_input_norm_weight", "up_proj", "w1", "w2",
+                                    "w1_mx", "w1_mx_scale", "w2_mx", "w2_mx_scale")]
 
 
 ROUTING_FIELDS = ("expert_weights", "expert_indices", "batch_size_per_expert", "expert_offsets",
@@ -90,6 +93,7 @@ _experts_forward = _sig("moe_experts_forward", c_i32, _P(_CConfig), _P(_CWeights
 _combine = _sig("moe_combine", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp, c_vp)
 _latent_up = _sig("moe_latent_up", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp,
                   ctypes.c_size_t, c_vp)
+_mx_quantize = _sig("moe_mx_quantize", c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp)
 _accumulate_counts = _sig("moe_accumulate_expert_counts", c_i32, c_i32, c_vp, c_vp, c_vp)
 _load_imbalance = _sig("moe_load_imbalance", c_i32, c_i32, c_vp, c_vp, c_vp)
 _score_bias_update = _sig("moe_score_bias_update", c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp)
@@ -129,6 +133,7 @@ class MoEConfig:
     up_proj_input_norm_eps: float = 1e-5
     dtype: str = "bf16"
     capacity_factor: Optional[float] = None
+    expert_precision: str = "bf16"
 
     @classmethod
     def of(cls, cfg) -> "MoEConfig":
@@ -156,6 +161,7 @@ class MoEConfig:
         c.up_proj_input_norm_eps = float(self.up_proj_input_norm_eps)
         c.dtype = DTYPE[self.dtype]
         c.capacity_factor = float(self.capacity_factor or 0.0)
+        c.expert_precision = PRECISION[self.expert_precision]
         return c
 
     @property
@@ -226,6 +232,8 @@ def _c_weights(cfg: MoEConfig, w: dict) -> _CWeights:
         "score_bias": ((E,), torch.float32), "down_proj": ((cfg.latent_dim or 0, d), D),
         "norm_weight": ((cfg.latent_dim or 0,), torch.float32), "up_proj": ((d, cfg.latent_dim or 0), D),
         "w1": ((E, 2 * h, K), D), "w2": ((E, K, h), D),
+        "w1_mx": ((E, 2 * h, K), torch.uint8), "w1_mx_scale": ((E, 2 * h, K // 32), torch.uint8),
+        "w2_mx": ((E, K, h), torch.uint8), "w2_mx_scale": ((E, K, h // 32), torch.uint8),
     }
     for name, (shape, dt) in checks.items():
         t = w.get(name)
@@ -239,7 +247,18 @@ def _c_weights(cfg: MoEConfig, w: dict) -> _CWeights:
     cw.up_proj = _ptr(w.get("up_proj"))
     cw.w1 = _ptr(w.get("w1"))
     cw.w2 = _ptr(w.get("w2"))
+    for name in ("w1_mx", "w1_mx_scale", "w2_mx", "w2_mx_scale"):
+        setattr(cw, name, _ptr(w.get(name)))
     return cw
+
+
+def quantize_expert_weights(weights: dict) -> dict:
+    """The weights with MXFP8 copies of the expert matrices added (w1_mx / w1_mx_scale: W1 rows
+    along K; w2_mx / w2_mx_scale: W2 rows along h), as the MXFP8 experts read them."""
+    out = dict(weights)
+    out["w1_mx"], out["w1_mx_scale"] = mx_quantize(weights["w1"])
+    out["w2_mx"], out["w2_mx_scale"] = mx_quantize(weights["w2"])
+    return out
 
 
 def _routing_tensors(cfg: MoEConfig, T: int, device, want=ROUTING_FIELDS) -> dict:
@@ -273,6 +292,8 @@ class MoELayer:
         self.cfg = MoEConfig.of(cfg)
         self._c = self.cfg.to_c()
         _check(_config_validate(ctypes.byref(self._c)))
+        if self.cfg.expert_precision == "mxfp8" and weights.get("w1_mx") is None:
+            weights = quantize_expert_weights(weights)
         self.weights = weights
         self._cw = _c_weights(self.cfg, weights)
         self._ws = None
@@ -435,3 +456,18 @@ def score_bias_update(accumulator: torch.Tensor, score_bias: torch.Tensor, bias_
     out = torch.empty((), dtype=torch.float64, device=accumulator.device) if imbalance else None
     _check(_score_bias_update(E, float(bias_gamma), _ptr(accumulator), _ptr(score_bias), _ptr(out), _stream()))
     return out
+
+
+# --------------------------------------------------------------------------- MXFP8
+
+def mx_quantize(x: torch.Tensor):
+    """MXFP8 of bf16 rows (..., cols): (E4M3 codes (..., cols) uint8, E8M0 block scales
+    (..., cols / 32) uint8); blocks of 32 along the last axis."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("mx_quantize takes bfloat16 rows")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty((*x.shape[:-1], cols // 32), dtype=torch.uint8, device=x.device)
+    _check(_mx_quantize(rows, cols, _ptr(x.contiguous()), _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales

@@ -84,6 +84,13 @@ moe_status_t validate_config(const moe_config_t* c) {
     return fail(MOE_ERR_UNSUPPORTED, "expert width (latent_dim or d_model) above 16384 (bf16) / 8192 (f32)");
   if (c->d_model > (int64_t(1) << 30) || c->hidden_size > (int64_t(1) << 30))
     return fail(MOE_ERR_UNSUPPORTED, "dimension too large");
+  if (c->expert_precision != MOE_PRECISION_BF16 && c->expert_precision != MOE_PRECISION_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "unknown expert_precision");
+  if (c->expert_precision == MOE_PRECISION_MXFP8) {
+    if (c->dtype != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "MXFP8 experts need a bf16 layer");
+    if (K % 128 || c->hidden_size % 128)
+      return fail(MOE_ERR_UNSUPPORTED, "MXFP8 experts need the expert width and hidden_size to be multiples of 128");
+  }
   return ok();
 }
 
@@ -133,6 +140,7 @@ Layer make_layer(const moe_config_t* c, int64_t T) {
   ly.up_norm = c->up_proj_input_norm != 0;
   ly.norm_eps = c->up_proj_input_norm_eps;
   ly.capacity = expert_capacity(c->capacity_factor, c->top_k, T, c->num_experts);
+  ly.mx = c->expert_precision == MOE_PRECISION_MXFP8;
   return ly;
 }
 
@@ -162,7 +170,10 @@ int expert_variant(const Layer& ly) {
   const double mean = static_cast<double>(ly.T) * ly.k / ly.E;
   return gemm_bf16_pick_variant(mean);
 }
-int expert_tile_m(const Layer& ly) { return ly.bf16 ? gemm_bf16_tile_m(expert_variant(ly)) : kF32TileM; }
+int expert_tile_m(const Layer& ly) {
+  if (ly.mx) return gemm_mx_tile_m();
+  return ly.bf16 ? gemm_bf16_tile_m(expert_variant(ly)) : kF32TileM;
+}
 int dense_variant(int64_t rows) { return gemm_bf16_pick_variant(static_cast<double>(rows)); }
 // Latent projections of few tokens run on the skinny weight-streaming GEMM.
 bool uses_skinny(const Layer& ly) { return ly.bf16 && ly.L > 0 && ly.T <= kSkinnyMaxRows; }
@@ -178,7 +189,7 @@ struct Carve {
 
 struct WsLayout {
   size_t logits, rscratch, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, z, act, yassign,
-      skinny, skinny_bytes, total;
+      skinny, skinny_bytes, zq, zs, aq, as, total;
   int32_t tile_cap;
 };
 
@@ -210,6 +221,11 @@ WsLayout ws_layout(const Layer& ly) {
                                               gemm_skinny_partial_bytes(ly.T, ly.d, ly.L))
                                    : 0;
   w.skinny = c.take(w.skinny_bytes);
+  // MXFP8 experts: E4M3 codes and E8M0 block scales of z (T, K) and of the activation (A, h)
+  w.zq = c.take(ly.mx ? T * static_cast<size_t>(ly.K) : 0);
+  w.zs = c.take(ly.mx ? T * static_cast<size_t>(ly.K) / 32 : 0);
+  w.aq = c.take(ly.mx ? A * static_cast<size_t>(ly.h) : 0);
+  w.as = c.take(ly.mx ? A * static_cast<size_t>(ly.h) / 32 : 0);
   w.total = c.off;
   return w;
 }
@@ -246,7 +262,12 @@ moe_status_t check_weights(const moe_config_t* c, const moe_weights_t* w, bool r
     if ((st = need(w->down_proj, "weights->down_proj")) != MOE_OK) return st;
     if ((st = need(w->up_proj, "weights->up_proj")) != MOE_OK) return st;
   }
-  if (experts) {
+  if (experts && c->expert_precision == MOE_PRECISION_MXFP8) {
+    if ((st = need(w->w1_mx, "weights->w1_mx")) != MOE_OK) return st;
+    if ((st = need(w->w1_mx_scale, "weights->w1_mx_scale")) != MOE_OK) return st;
+    if ((st = need(w->w2_mx, "weights->w2_mx")) != MOE_OK) return st;
+    if ((st = need(w->w2_mx_scale, "weights->w2_mx_scale")) != MOE_OK) return st;
+  } else if (experts) {
     if ((st = need(w->w1, "weights->w1")) != MOE_OK) return st;
     if ((st = need(w->w2, "weights->w2")) != MOE_OK) return st;
   }
@@ -275,8 +296,76 @@ hipError_t run_dense(const Layer& ly, int64_t rows, const void* A, int64_t lda, 
   return launch_gemm_f32(c, false, nullptr, s);
 }
 
+// Workspace of the MXFP8 experts: codes and block scales of z and of the activation.
+struct MxBuffers {
+  uint8_t* zq;
+  uint8_t* zs;
+  uint8_t* aq;
+  uint8_t* as;
+};
+
+MxBuffers mx_buffers(void* ws, const WsLayout& L) {
+  return MxBuffers{at<uint8_t>(ws, L.zq), at<uint8_t>(ws, L.zs), at<uint8_t>(ws, L.aq), at<uint8_t>(ws, L.as)};
+}
+
+// MXFP8 experts: quantise z, GEMM1 (+ SwiGLU, bf16 activation), quantise the activation, GEMM2.
+hipError_t run_experts_mx(const Layer& ly, const void* z, const int32_t* perm, const TileList& tiles,
+                          const moe_weights_t* w, void* act, void* yassign, const MxBuffers& mb, hipStream_t s) {
+  const int64_t A = ly.T * ly.k;
+  hipError_t e;
+  if ((e = launch_mx_quantize(z, ly.T, ly.K, mb.zq, mb.zs, s)) != hipSuccess) return e;
+  GemmCall g1{};
+  g1.A = mb.zq;
+  g1.lda = ly.K;
+  g1.a_scale = mb.zs;
+  g1.a_scale_ld = ly.K / 32;
+  g1.gather = perm;
+  g1.gather_div = ly.k;
+  g1.B = w->w1_mx;
+  g1.ldb = ly.K;
+  g1.b_group_stride = 2 * ly.h * ly.K;
+  g1.b_scale = w->w1_mx_scale;
+  g1.b_scale_ld = ly.K / 32;
+  g1.b_scale_group_stride = 2 * ly.h * (ly.K / 32);
+  g1.C = act;
+  g1.ldc = ly.h;
+  g1.N = ly.h;
+  g1.Kd = ly.K;
+  g1.swiglu_h = ly.h;
+  g1.tiles = tiles;
+  g1.a_rows = ly.T;
+  g1.c_rows = A;
+  g1.rows_bound = A;
+  if ((e = launch_gemm_mx(g1, s)) != hipSuccess) return e;
+  if ((e = launch_mx_quantize(act, A, ly.h, mb.aq, mb.as, s)) != hipSuccess) return e;
+  GemmCall g2{};
+  g2.A = mb.aq;
+  g2.lda = ly.h;
+  g2.a_scale = mb.as;
+  g2.a_scale_ld = ly.h / 32;
+  g2.B = w->w2_mx;
+  g2.ldb = ly.h;
+  g2.b_group_stride = ly.K * ly.h;
+  g2.b_scale = w->w2_mx_scale;
+  g2.b_scale_ld = ly.h / 32;
+  g2.b_scale_group_stride = ly.K * (ly.h / 32);
+  g2.C = yassign;
+  g2.ldc = ly.K;
+  g2.scatter = perm;
+  g2.N = ly.K;
+  g2.Kd = ly.h;
+  g2.tiles = tiles;
+  g2.a_rows = A;
+  g2.c_rows = A;
+  g2.rows_bound = A;
+  return launch_gemm_mx(g2, s);
+}
+
 hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, const TileList& tiles,
-                       const void* w1, const void* w2, void* act, void* yassign, hipStream_t s) {
+                       const moe_weights_t* w, void* act, void* yassign, const MxBuffers& mb, hipStream_t s) {
+  if (ly.mx) return run_experts_mx(ly, z, perm, tiles, w, act, yassign, mb, s);
+  const void* w1 = w->w1;
+  const void* w2 = w->w2;
   const int64_t A = ly.T * ly.k;
   GemmCall g1{};
   g1.A = z;
@@ -449,7 +538,7 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
                 "latent down");
     z = at<void>(ws, L.z);
   }
-  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), at<void>(ws, L.yassign), s),
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w, at<void>(ws, L.act), at<void>(ws, L.yassign), mx_buffers(ws, L), s),
               "experts");
   MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, at<void>(ws, L.yassign), s), "dropped rows");
   if (ly.L) {
@@ -575,7 +664,7 @@ moe_status_t moe_experts_forward(const moe_config_t* c, const moe_weights_t* w, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const TileList tiles = tiles_of(ws, L);
   MOE_TRY_HIP(launch_build_tiles(ly, offsets, tiles, expert_tile_m(ly), s), "tile list");
-  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w->w1, w->w2, at<void>(ws, L.act), y_assign, s), "experts");
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w, at<void>(ws, L.act), y_assign, mx_buffers(ws, L), s), "experts");
   MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, y_assign, s), "dropped rows");
   return ok();
 }
@@ -619,6 +708,21 @@ moe_status_t moe_latent_up(const moe_config_t* c, const moe_weights_t* w, int64_
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------ MXFP8
+
+extern "C" moe_status_t moe_mx_quantize(int64_t rows, int64_t cols, const void* x, uint8_t* codes,
+                                        uint8_t* scales, void* stream) {
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows must be >= 0");
+  if (cols <= 0 || cols % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "cols must be a positive multiple of 32");
+  if (rows == 0) return ok();
+  moe_status_t st;
+  if ((st = need(x, "x")) != MOE_OK) return st;
+  if ((st = need(codes, "codes")) != MOE_OK) return st;
+  if ((st = need(scales, "scales")) != MOE_OK) return st;
+  MOE_TRY_HIP(launch_mx_quantize(x, rows, cols, codes, scales, static_cast<hipStream_t>(stream)), "mx quantize");
+  return ok();
+}
 
 // ------------------------------------------------------------------------ balancing state
 

@@ -123,6 +123,7 @@ struct Layer {
   bool up_norm;
   float norm_eps;
   int64_t capacity;  // expert capacity (token dropping); 0 = dropless
+  bool mx;           // MXFP8 expert matmuls
 };
 
 // Per-expert M-tile list consumed by the grouped GEMMs (device memory, built on the device).
@@ -190,6 +191,13 @@ struct GemmCall {
   int64_t swiglu_h;         // > 0: SwiGLU epilogue, gate rows start at +swiglu_h
   int64_t dense_M;          // > 0: dense GEMM with this many rows (tiles ignored)
   TileList tiles;           // grouped mode
+  // MXFP8 operands (launch_gemm_mx): E8M0 scale bytes, one per 32 elements along Kd, rows
+  // laid out like the operands' rows (scale row stride *_scale_ld = Kd / 32 bytes)
+  const uint8_t* a_scale;
+  int64_t a_scale_ld;
+  const uint8_t* b_scale;
+  int64_t b_scale_ld;
+  int64_t b_scale_group_stride;  // scale bytes between consecutive experts' weights
   // Bounds used to clamp every row index a kernel derives from device data, so that a
   // corrupt index can never address memory outside the operands.
   int64_t a_rows;           // rows of A
@@ -201,6 +209,11 @@ struct GemmCall {
 int gemm_bf16_tile_m(int variant);
 int gemm_bf16_pick_variant(double mean_rows_per_group);
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s);
+// Grouped MXFP8 GEMM: A and B are E4M3 codes (1 byte per element, ld in elements = bytes)
+// with E8M0 scales; Kd a multiple of 128; M-tile height gemm_mx_tile_m(). Output and
+// epilogues as launch_gemm_bf16 (SwiGLU + gather, or scatter).
+int gemm_mx_tile_m();
+hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s);
 // Dense C(f32) = A(bf16) x sum_p B_p(bf16)^T over planes p = 0..2 (B_p at B + p*b_plane_stride):
 // the fp32-exact router contraction. N must be a multiple of 4; N-tile width below.
 hipError_t launch_gemm_bf16_planes_f32(const GemmCall& c, hipStream_t s);
@@ -227,6 +240,11 @@ hipError_t launch_accumulate_counts(int E, const int32_t* counts, int64_t* acc, 
 hipError_t launch_load_imbalance(int E, const int64_t* counts, double* out, hipStream_t s);
 hipError_t launch_score_bias_update(int E, float gamma, int64_t* acc, float* bias, double* imbalance,
                                     hipStream_t s);
+
+// MXFP8 quantisation of bf16 rows: x (rows, cols) -> E4M3 codes (rows, cols) and E8M0 block
+// scales (rows, cols / 32); cols a multiple of 32.
+hipError_t launch_mx_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
 
 // Weighted combine (+ RMSNorm): out (T, K) D.
 hipError_t launch_combine(const Layer& ly, const void* y_assign, const float* w,

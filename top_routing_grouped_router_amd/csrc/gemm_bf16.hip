@@ -42,18 +42,24 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 
-template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_, int PLANES_ = 1>
+template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_, int PLANES_ = 1, int EB_ = 2>
 struct Shape {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  // Bytes per operand element: 2 = bf16; 1 = MXFP8 (E4M3 codes with one E8M0 scale byte per
+  // 32 elements along k, multiplied on v_mfma_scale_f32_32x32x64_f8f6f4).
+  static constexpr int EB = EB_;
+  static constexpr bool MX = EB == 1;
   // Weight planes summed into one product (3 for the fp32 router: its weights split exactly
   // into three bf16 planes); each stage then stages PLANES x BN weight rows.
   static constexpr int PLANES = PLANES_;
   static constexpr int BK = BK_;                // k per pipeline stage
-  static constexpr int ROWB = BK * 2;           // bytes per staged row
+  static constexpr int ROWB = BK * EB;          // bytes per staged row
   static constexpr int CHUNKS = ROWB / 16;      // 16-byte chunks per staged row
   static constexpr int ROWS_PER_BANKLINE = 256 / ROWB;  // rows sharing the 64 LDS banks
   static constexpr int kRowsPerDma = 1024 / ROWB;       // rows one wave-wide 16-byte DMA load fills
@@ -67,8 +73,15 @@ struct Shape {
   static constexpr int NI = (BM + BROWS) / kRowsPerDma;  // DMA loads per stage
   static constexpr int NQ = (NI + NW - 1) / NW;        // per wavefront (upper bound)
   static constexpr int NQMIN = NI / NW;                // per wavefront (lower bound)
-  static constexpr int STAGE = (BM + BROWS) * ROWB;
+  static constexpr int DATA = (BM + BROWS) * ROWB;  // operand bytes per stage
+  // MXFP8: the stage's scale bytes follow the operands, 4 per staged row (k-stage 128 = four
+  // blocks of 32); one 4-byte-per-lane DMA load per 64 rows.
+  static constexpr int SCB = MX ? BK / 32 : 0;
+  static constexpr int NSC = MX ? (BM + BROWS) / 64 : 0;
+  static constexpr int STAGE = DATA + (BM + BROWS) * SCB;
   static constexpr int LDS = NSTAGE * STAGE;
+  static_assert(!MX || (BK == 128 && PLANES == 1 && BM % 64 == 0 && BN % 64 == 0 && NSC <= NW),
+                "MXFP8 stages: 128-element k-stages, 64-row scale loads, one per wavefront");
   static_assert(BM % kRowsPerDma == 0 && BN % kRowsPerDma == 0, "whole DMA loads per tile");
   static_assert(BK % 16 == 0 && CHUNKS >= 2 && CHUNKS <= 8, "stage depth");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "vmcnt bookkeeping covers 2..4 stages");
@@ -83,6 +96,9 @@ using ShapeLarge = Shape<2, 4, 4, 2, 64, 2, 1>;
 // 64 x 256 tile, 4 wavefronts (1 x 4) of 64 x 64: few rows per expert (decode-shaped loads);
 // 2 stages x 40 KiB, two workgroups per CU.
 using ShapeSmall = Shape<1, 4, 2, 2, 64, 2, 2>;
+// MXFP8 expert GEMMs: the large tile with 128-element k-stages (one 128-byte line of E4M3 codes
+// per row) plus the rows' scale bytes; 2 stages x 66 KiB.
+using ShapeLargeMX = Shape<2, 4, 4, 2, 128, 2, 1, 1, 1>;
 // Router logits: 256 tokens x 128 experts x 3 weight planes, 8 wavefronts (2 x 4) of 128 x 32;
 // 2 stages x 80 KiB (the whole LDS).
 using ShapeRouter = Shape<2, 4, 4, 1, 64, 2, 1, 3>;
@@ -137,6 +153,15 @@ __device__ __forceinline__ void sched_stage_step() {
   }
 }
 
+// One MXFP8 MFMA: a and b hold 32 E4M3 codes of a row per lane (bytes 0-15 from the first
+// 32-element block of the 64-k step, bytes 16-31 from the second: each lane supplies its half
+// of both blocks), sa / sb the E8M0 scale of block (lane / 32) of the lane's row (lane % 32)
+// in byte 0.
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, static_cast<int>(sa), 0,
+                                                         static_cast<int>(sb));
+}
+
 template <int KSTEPS, int KREADS, int KMFMA, int KLOADS>
 __device__ __forceinline__ void sched_stage() {
   __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);  // step-0 reads
@@ -178,6 +203,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     int rows;
     const unsigned char* Bexp;
     uint32_t src_off[S::NQ];  // byte offset of the source 16-byte chunk of load q (k-stage 0)
+    const unsigned char* sc_base;  // MXFP8: scale array of this wavefront's 64 staged rows
+    uint32_t sc_off;               // MXFP8: byte offset of this lane's row scales (k-stage 0)
   };
   // The load index inside a stage is uniform per wavefront, so is the operand it reads.
   auto load_is_a = [&](int q) { return wave + S::NW * q < S::BM / S::kRowsPerDma; };
@@ -201,7 +228,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       t.rows = c.tiles.rows[mt];
       grp = c.tiles.expert[mt];
     }
-    t.Bexp = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(c.B) + grp * c.b_group_stride);
+    t.Bexp = static_cast<const unsigned char*>(c.B) + grp * c.b_group_stride * S::EB;
 #pragma unroll
     for (int q = 0; q < S::NQ; ++q) {
       const int i = wave + S::NW * q;
@@ -214,7 +241,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         p = min(max(p, int64_t(0)), c.rows_bound - 1);
         int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
         src = min(max(src, int64_t(0)), c.a_rows - 1);
-        t.src_off[q] = static_cast<uint32_t>(src * c.lda * 2 + chunk_l * 16);
+        t.src_off[q] = static_cast<uint32_t>(src * c.lda * S::EB + chunk_l * 16);
       } else {
         int64_t wrow;
         // weight rows of plane p follow those of plane p-1
@@ -229,7 +256,36 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           wrow = min(t.nt * S::BN + rp, c.N - 1);
         }
         const int64_t pbase = S::PLANES == 1 ? 0 : plane * c.b_plane_stride;
-        t.src_off[q] = static_cast<uint32_t>((pbase + wrow * c.ldb) * 2 + chunk_l * 16);
+        t.src_off[q] = static_cast<uint32_t>((pbase + wrow * c.ldb) * S::EB + chunk_l * 16);
+      }
+    }
+    if constexpr (S::MX) {
+      // wavefront w < NSC loads the scales of staged rows [64 w, 64 w + 64): token rows first,
+      // then weight rows, the same rows (and padding clamps) as the operand loads above
+      if (wave < S::NSC) {
+        const int r = wave * 64 + lane;
+        if (r < S::BM) {
+          int64_t p = t.row0 + (r < t.rows ? r : 0);
+          p = min(max(p, int64_t(0)), c.rows_bound - 1);
+          int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
+          src = min(max(src, int64_t(0)), c.a_rows - 1);
+          t.sc_base = c.a_scale;
+          t.sc_off = static_cast<uint32_t>(src * c.a_scale_ld);
+        } else {
+          const int rp = r - S::BM;
+          int64_t wrow;
+          if (SWIGLU) {
+            const int wv = rp / (S::TN * 32), qq = rp % (S::TN * 32);
+            const int half = qq / (S::TN * 16);
+            int64_t col = t.nt * (S::BN / 2) + wv * (S::TN * 16) + (qq % (S::TN * 16));
+            col = min(col, c.N - 1);
+            wrow = col + (half ? c.swiglu_h : 0);
+          } else {
+            wrow = min(t.nt * S::BN + rp, c.N - 1);
+          }
+          t.sc_base = c.b_scale + grp * c.b_scale_group_stride;
+          t.sc_off = static_cast<uint32_t>(wrow * c.b_scale_ld);
+        }
       }
     }
   };
@@ -245,10 +301,49 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           (load_is_a(q) ? Ab : t.Bexp) + (t.src_off[q] + static_cast<uint32_t>(kt) * S::ROWB);
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
     }
+    if constexpr (S::MX) {
+      if (wave < S::NSC)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(t.sc_base + (t.sc_off + static_cast<uint32_t>(kt) * 4)),
+                                         LDS_PTR(st + S::DATA + wave * 256), 4, 0, 0);
+    }
   };
 
   f32x16 acc[S::TM][S::TN];
-  bf16x8 fw[2][S::PLANES][S::TN], ft[2][S::TM];
+  bf16x8 fw[S::MX ? 1 : 2][S::PLANES][S::TN], ft[S::MX ? 1 : 2][S::TM];
+  // MXFP8 operands: 32 codes per lane (two 16-byte chunks: the lane's halves of the two
+  // 32-element blocks of a 64-k step) and the scale words of the stage
+  i32x8 fwx[S::MX ? 2 : 1][S::TN], ftx[S::MX ? 2 : 1][S::TM];
+  uint32_t scw[S::TN], sct[S::TM];
+  auto lds_frags_mx = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
+    const int c0 = 4 * kk + (lane >> 5), c1 = c0 + 2;
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) {
+      const int row = wn * S::TN * 32 + j * 32 + (lane & 31);
+      const u32x4v lo = *reinterpret_cast<const u32x4v*>(lb + swz<S>(row, c0));
+      const u32x4v hi = *reinterpret_cast<const u32x4v*>(lb + swz<S>(row, c1));
+      fwx[fs][j] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                         static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    }
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) {
+      const int row = wm * S::TM * 32 + i * 32 + (lane & 31);
+      const u32x4v lo = *reinterpret_cast<const u32x4v*>(la + swz<S>(row, c0));
+      const u32x4v hi = *reinterpret_cast<const u32x4v*>(la + swz<S>(row, c1));
+      ftx[fs][i] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                         static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    }
+  };
+  // scale bytes [b0 b1 b2 b3] of the stage's four blocks, shifted so that byte 0 is block
+  // (lane / 32) (64-k step 0) and byte 2 block 2 + (lane / 32) (step 1)
+  auto lds_scales = [&](const unsigned char* scl) {
+    const int shift = 8 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+      scw[j] = *reinterpret_cast<const uint32_t*>(scl + (S::BM + wn * S::TN * 32 + j * 32 + (lane & 31)) * 4) >> shift;
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i)
+      sct[i] = *reinterpret_cast<const uint32_t*>(scl + (wm * S::TM * 32 + i * 32 + (lane & 31)) * 4) >> shift;
+  };
   auto lds_frags = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
     const int ch = 2 * kk + (lane >> 5);
 #pragma unroll
@@ -411,22 +506,37 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // k16 steps with fragments double-buffered in registers; the directives interleave step
       // kk+1's LDS reads with step kk's MFMAs so the matrix pipe does not wait on an LDS round
       // trip before every MFMA group.
-      constexpr int kSteps = S::BK / 16;
-      constexpr int kReads = S::TM + S::PLANES * S::TN;  // LDS fragment reads per k16 step
-      constexpr int kMfma = S::TM * S::TN * S::PLANES;   // MFMAs per k16 step
-      lds_frags(0, la, lb, 0);
+      if constexpr (S::MX) {
+        // two 64-k steps per 128-element stage; scale words read once per stage
+        lds_scales(la + S::DATA);
+        lds_frags_mx(0, la, lb, 0);
 #pragma unroll
-      for (int kk = 0; kk < kSteps; ++kk) {
-        if (kk + 1 < kSteps) lds_frags((kk + 1) & 1, la, lb, kk + 1);
+        for (int kk = 0; kk < S::BK / 64; ++kk) {
+          if (kk + 1 < S::BK / 64) lds_frags_mx((kk + 1) & 1, la, lb, kk + 1);
 #pragma unroll
-        for (int i = 0; i < S::TM; ++i)
+          for (int i = 0; i < S::TM; ++i)
 #pragma unroll
-          for (int j = 0; j < S::TN; ++j)
+            for (int j = 0; j < S::TN; ++j)
+              acc[i][j] = mfma_mx(fwx[kk & 1][j], ftx[kk & 1][i], acc[i][j], scw[j] >> (16 * kk), sct[i] >> (16 * kk));
+        }
+      } else {
+        constexpr int kSteps = S::BK / 16;
+        constexpr int kReads = S::TM + S::PLANES * S::TN;  // LDS fragment reads per k16 step
+        constexpr int kMfma = S::TM * S::TN * S::PLANES;   // MFMAs per k16 step
+        lds_frags(0, la, lb, 0);
 #pragma unroll
-            for (int pl = S::PLANES - 1; pl >= 0; --pl)  // smallest plane first
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk & 1][pl][j], ft[kk & 1][i], acc[i][j], 0, 0, 0);
+        for (int kk = 0; kk < kSteps; ++kk) {
+          if (kk + 1 < kSteps) lds_frags((kk + 1) & 1, la, lb, kk + 1);
+#pragma unroll
+          for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+              for (int pl = S::PLANES - 1; pl >= 0; --pl)  // smallest plane first
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk & 1][pl][j], ft[kk & 1][i], acc[i][j], 0, 0, 0);
+        }
+        sched_stage<kSteps, kReads, kMfma, 0>();
       }
-      sched_stage<kSteps, kReads, kMfma, 0>();
     }
     // Every wavefront done reading this tile's last stages: slot 0 is free for the next tile.
     wait_lgkmcnt0();
@@ -491,6 +601,13 @@ hipError_t launch_gemm_bf16_planes_f32(const GemmCall& c, hipStream_t s) {
 }
 
 int gemm_bf16_pick_variant(double mean_rows_per_group) { return mean_rows_per_group >= 96.0 ? 0 : 1; }
+
+int gemm_mx_tile_m() { return ShapeLargeMX::BM; }
+
+hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s) {
+  if (c.dense_M > 0 || c.Kd % ShapeLargeMX::BK != 0 || !c.a_scale || !c.b_scale) return hipErrorInvalidValue;
+  return launch_shape<ShapeLargeMX>(c, s, ShapeLargeMX::WG_PER_CU);
+}
 
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s) {
   if (variant == 0) return launch_shape<ShapeLarge>(c, s, ShapeLarge::WG_PER_CU);
