@@ -165,15 +165,18 @@ moe_status_t check_tokens(const moe_config_t* c, int64_t T) {
 
 size_t elem_size(const Layer& ly) { return ly.bf16 ? 2 : 4; }
 
-// M-tile height the expert GEMMs use for this layer and token count.
-int expert_variant(const Layer& ly) {
-  const double mean = static_cast<double>(ly.T) * ly.k / ly.E;
-  return gemm_bf16_pick_variant(mean);
+// How the expert GEMMs cut each expert's rows into M-tiles. bf16: the large shape's 256-row
+// tiles, with remainders of at most 128 rows in 64-row tiles of the small shape (a second
+// launch); fp32 and MXFP8: one list of their single shape.
+constexpr int kSmallRemainderMax = 128;
+TilePlan tile_plan(const Layer& ly) {
+  if (ly.mx) return TilePlan{gemm_mx_tile_m(), gemm_mx_tile_m(), 0};
+  if (!ly.bf16) return TilePlan{kF32TileM, kF32TileM, 0};
+  return TilePlan{gemm_bf16_tile_m(0), gemm_bf16_tile_m(1), kSmallRemainderMax};
 }
-int expert_tile_m(const Layer& ly) {
-  if (ly.mx) return gemm_mx_tile_m();
-  return ly.bf16 ? gemm_bf16_tile_m(expert_variant(ly)) : kF32TileM;
-}
+// No expert receives more than T rows: with T at most the largest remainder every expert's
+// rows go to the remainder list and the main list is empty.
+bool main_list_empty(const Layer& ly, const TilePlan& p) { return p.small_max > 0 && ly.T <= p.small_max; }
 int dense_variant(int64_t rows) { return gemm_bf16_pick_variant(static_cast<double>(rows)); }
 // Latent projections of few tokens run on the skinny weight-streaming GEMM.
 bool uses_skinny(const Layer& ly) { return ly.bf16 && ly.L > 0 && ly.T <= kSkinnyMaxRows; }
@@ -188,9 +191,9 @@ struct Carve {
 };
 
 struct WsLayout {
-  size_t logits, rscratch, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, z, act, yassign,
-      skinny, skinny_bytes, zq, zs, aq, as, total;
-  int32_t tile_cap;
+  size_t logits, rscratch, idx, w, counts, offsets, perm, inv, scratch, tcount, texpert, trow0, trows, scount,
+      sexpert, srow0, srows, z, act, yassign, skinny, skinny_bytes, zq, zs, aq, as, total;
+  int32_t tile_cap, small_cap;
 };
 
 WsLayout ws_layout(const Layer& ly) {
@@ -198,8 +201,10 @@ WsLayout ws_layout(const Layer& ly) {
   Carve c;
   const size_t T = static_cast<size_t>(ly.T), E = static_cast<size_t>(ly.E), A = T * ly.k;
   const size_t es = elem_size(ly);
-  const int bm = expert_tile_m(ly);
-  w.tile_cap = static_cast<int32_t>((A + bm - 1) / bm + E);
+  const TilePlan plan = tile_plan(ly);
+  w.tile_cap = static_cast<int32_t>((A + plan.bm - 1) / plan.bm + E);
+  // at most ceil(small_max / bs) remainder tiles per expert
+  w.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs)) : 0;
   w.logits = c.take(static_cast<size_t>(router_splits(ly)) * T * E * 4);  // logit partial sums
   w.rscratch = c.take(router_scratch_bytes(ly));                            // router weight planes
   w.idx = c.take(A * 4);
@@ -213,6 +218,10 @@ WsLayout ws_layout(const Layer& ly) {
   w.texpert = c.take(static_cast<size_t>(w.tile_cap) * 4);
   w.trow0 = c.take(static_cast<size_t>(w.tile_cap) * 4);
   w.trows = c.take(static_cast<size_t>(w.tile_cap) * 4);
+  w.scount = c.take(4);
+  w.sexpert = c.take(static_cast<size_t>(w.small_cap) * 4);
+  w.srow0 = c.take(static_cast<size_t>(w.small_cap) * 4);
+  w.srows = c.take(static_cast<size_t>(w.small_cap) * 4);
   w.z = c.take(ly.L ? T * static_cast<size_t>(ly.L) * es : 0);
   w.act = c.take(A * static_cast<size_t>(ly.h) * es);
   w.yassign = c.take(A * static_cast<size_t>(ly.K) * es);
@@ -242,6 +251,16 @@ TileList tiles_of(void* ws, const WsLayout& w) {
   t.row0 = at<int32_t>(ws, w.trow0);
   t.rows = at<int32_t>(ws, w.trows);
   t.cap = w.tile_cap;
+  return t;
+}
+
+TileList small_tiles_of(void* ws, const WsLayout& w) {
+  TileList t;
+  t.count = at<int32_t>(ws, w.scount);
+  t.expert = at<int32_t>(ws, w.sexpert);
+  t.row0 = at<int32_t>(ws, w.srow0);
+  t.rows = at<int32_t>(ws, w.srows);
+  t.cap = w.small_cap;
   return t;
 }
 
@@ -362,7 +381,8 @@ hipError_t run_experts_mx(const Layer& ly, const void* z, const int32_t* perm, c
 }
 
 hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, const TileList& tiles,
-                       const moe_weights_t* w, void* act, void* yassign, const MxBuffers& mb, hipStream_t s) {
+                       const TileList& small_tiles, const moe_weights_t* w, void* act, void* yassign,
+                       const MxBuffers& mb, hipStream_t s) {
   if (ly.mx) return run_experts_mx(ly, z, perm, tiles, w, act, yassign, mb, s);
   const void* w1 = w->w1;
   const void* w2 = w->w2;
@@ -401,9 +421,17 @@ hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, cons
   g2.rows_bound = A;
   hipError_t e;
   if (ly.bf16) {
-    const int v = expert_variant(ly);
-    if ((e = launch_gemm_bf16(g1, v, s)) != hipSuccess) return e;
-    return launch_gemm_bf16(g2, v, s);
+    // main list on the large shape, remainders on the small shape (each GEMM's two launches
+    // cover disjoint rows)
+    const TilePlan plan = tile_plan(ly);
+    const bool run_main = !main_list_empty(ly, plan);
+    GemmCall g1s = g1, g2s = g2;
+    g1s.tiles = small_tiles;
+    g2s.tiles = small_tiles;
+    if (run_main && (e = launch_gemm_bf16(g1, 0, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16(g1s, 1, s)) != hipSuccess) return e;
+    if (run_main && (e = launch_gemm_bf16(g2, 0, s)) != hipSuccess) return e;
+    return launch_gemm_bf16(g2s, 1, s);
   }
   if ((e = launch_gemm_f32(g1, false, nullptr, s)) != hipSuccess) return e;
   return launch_gemm_f32(g2, false, nullptr, s);
@@ -523,13 +551,14 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
   int32_t* perm = r.permutation ? r.permutation : at<int32_t>(ws, L.perm);
   int32_t* inv = r.inverse_permutation ? r.inverse_permutation : at<int32_t>(ws, L.inv);
   const TileList tiles = tiles_of(ws, L);
+  const TileList small_tiles = small_tiles_of(ws, L);
 
   MOE_TRY_HIP(launch_router_logits(ly, x, w->router_weight, parts, nsplit, at<void>(ws, L.rscratch), s), "router logits");
   MOE_TRY_HIP(launch_gate_topk(ly, parts, nsplit, false, w->score_bias, ly.router_bias ? w->router_bias : nullptr,
                                idx, wts, r.router_scores, r.router_logits, s),
               "gating/top-k");
-  MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles,
-                              expert_tile_m(ly), s),
+  MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles, small_tiles,
+                              tile_plan(ly), s),
               "dispatch");
   const void* z = x;
   if (ly.L) {
@@ -538,7 +567,8 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
                 "latent down");
     z = at<void>(ws, L.z);
   }
-  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w, at<void>(ws, L.act), at<void>(ws, L.yassign), mx_buffers(ws, L), s),
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, small_tiles, w, at<void>(ws, L.act), at<void>(ws, L.yassign),
+                          mx_buffers(ws, L), s),
               "experts");
   MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, at<void>(ws, L.yassign), s), "dropped rows");
   if (ly.L) {
@@ -619,7 +649,7 @@ moe_status_t moe_permute(const moe_config_t* c, int64_t T, const int32_t* idx, i
   if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   if ((st = need(idx, "expert_indices")) != MOE_OK) return st;
   MOE_TRY_HIP(launch_dispatch(ly, idx, counts, offsets, perm, inv, at<void>(ws, L.scratch), tiles_of(ws, L),
-                              expert_tile_m(ly), s),
+                              small_tiles_of(ws, L), tile_plan(ly), s),
               "dispatch");
   return ok();
 }
@@ -663,8 +693,10 @@ moe_status_t moe_experts_forward(const moe_config_t* c, const moe_weights_t* w, 
   if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const TileList tiles = tiles_of(ws, L);
-  MOE_TRY_HIP(launch_build_tiles(ly, offsets, tiles, expert_tile_m(ly), s), "tile list");
-  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, w, at<void>(ws, L.act), y_assign, mx_buffers(ws, L), s), "experts");
+  const TileList small_tiles = small_tiles_of(ws, L);
+  MOE_TRY_HIP(launch_build_tiles(ly, offsets, tiles, small_tiles, tile_plan(ly), s), "tile list");
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, small_tiles, w, at<void>(ws, L.act), y_assign, mx_buffers(ws, L), s),
+              "experts");
   MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, y_assign, s), "dropped rows");
   return ok();
 }

@@ -135,6 +135,17 @@ struct TileList {
   int32_t cap;
 };
 
+// How an expert's rows are cut into M-tiles: full tiles of bm rows; the remainder r = rows % bm
+// goes to one more tile of that list when r > small_max, else to ceil(r / bs) tiles of bs rows
+// in a second list, run by the smaller tile shape (small_max = 0: one list only). With the
+// large shape's 256-row tiles, an expert of 1 + 4 * 256 rows then adds one 64-row tile to the
+// small list instead of a 256-row tile that is almost all padding.
+struct TilePlan {
+  int bm;         // rows per tile of the main list
+  int bs;         // rows per tile of the remainder list
+  int small_max;  // largest remainder sent to the remainder list (0 = none)
+};
+
 // Grid-wide properties cached per device.
 int device_cu_count();
 
@@ -160,18 +171,18 @@ hipError_t launch_gate_topk(const Layer& ly, const float* input, int nsplit, boo
                             const float* score_bias, const float* router_bias, int32_t* idx, float* w,
                             float* scores_out, float* logits_out, hipStream_t s);
 
-// Histogram, stable permutation and the M-tile list (tile height bm).
+// Histogram, stable permutation and the M-tile lists (main and remainder, see TilePlan).
 size_t dispatch_scratch_bytes(const Layer& ly);
 hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
-                           int bm, hipStream_t s);
+                           const TileList& small_tiles, const TilePlan& plan, hipStream_t s);
 // With a capacity (ly.capacity > 0): zero the expert-output rows (assignment order, K wide) of
 // the dropped assignments, i.e. rows perm[p] for sorted positions p in [offsets[E], T*k).
 hipError_t launch_zero_dropped(const Layer& ly, const int32_t* offsets, const int32_t* perm, void* y,
                                hipStream_t s);
 // Only the M-tile list, from existing offsets.
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
-                              int bm, hipStream_t s);
+                              const TileList& small_tiles, const TilePlan& plan, hipStream_t s);
 
 // GEMM variants. All operands are "NT": A (rows, Kd) and B (N, Kd), Kd contiguous.
 struct GemmCall {

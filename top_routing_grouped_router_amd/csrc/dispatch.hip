@@ -118,13 +118,46 @@ __global__ __launch_bounds__(256) void scan_cols_kernel(int32_t* __restrict__ bl
   if (threadIdx.x == 0) counts[e] = carry;
 }
 
-// counts -> offsets (or offsets given) -> M-tile list. One block of 1024 threads, E <= 1024.
+// Tiles of one expert with c rows under a plan: nb in the main list, ns in the remainder list.
+__device__ __forceinline__ void expert_tile_counts(int c, const TilePlan& p, int& nb, int& ns) {
+  const int full = c / p.bm, r = c - full * p.bm;
+  if (r == 0 || r > p.small_max) {
+    nb = full + (r > 0 ? 1 : 0);
+    ns = 0;
+  } else {
+    nb = full;
+    ns = (r + p.bs - 1) / p.bs;
+  }
+}
+
+// Writes expert e's tiles (rows [excl, excl + c) of the sorted order) at list positions tb / ts.
+__device__ __forceinline__ void write_expert_tiles(int e, int excl, int c, const TilePlan& p, int nb, int ns,
+                                                   int tb, int ts, const TileList& big, const TileList& small) {
+  for (int i = 0; i < nb; ++i) {
+    const int ti = tb + i;
+    if (ti >= big.cap) break;
+    big.expert[ti] = e;
+    big.row0[ti] = excl + i * p.bm;
+    big.rows[ti] = min(p.bm, c - i * p.bm);
+  }
+  const int r0 = nb * p.bm;
+  for (int i = 0; i < ns; ++i) {
+    const int ti = ts + i;
+    if (ti >= small.cap) break;
+    small.expert[ti] = e;
+    small.row0[ti] = excl + r0 + i * p.bs;
+    small.rows[ti] = min(p.bs, c - r0 - i * p.bs);
+  }
+}
+
+// counts -> offsets (or offsets given) -> M-tile lists. One block of 1024 threads, E <= 1024.
 // With a capacity (> 0) the offsets are those of the kept counts min(count, capacity), and
 // drop_off (E + 1) receives the exclusive scan of the dropped counts.
 __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __restrict__ counts_in,
                                                              const int32_t* __restrict__ offsets_in,
                                                              int32_t* __restrict__ offsets_out,
-                                                             int E, int bm, TileList tiles, int capacity,
+                                                             int E, TilePlan plan, TileList tiles,
+                                                             TileList small_tiles, int capacity,
                                                              int32_t* __restrict__ drop_off) {
   __shared__ int sh[17];
   const int e = threadIdx.x;
@@ -151,18 +184,20 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
   }
   if (tiles.cap <= 0) return;
   c = c < 0 ? 0 : c;
-  const int mt = (c + bm - 1) / bm;
-  const int tbase = block_inclusive_scan(mt, sh) - mt;
+  int nb = 0, ns = 0;
+  if (e < E) expert_tile_counts(c, plan, nb, ns);
+  const int tb = block_inclusive_scan(nb, sh) - nb;
   __syncthreads();
   const int total = sh[16];
-  for (int i = 0; i < mt; ++i) {
-    const int ti = tbase + i;
-    if (ti >= tiles.cap) break;
-    tiles.expert[ti] = e;
-    tiles.row0[ti] = excl + i * bm;
-    tiles.rows[ti] = min(bm, c - i * bm);
+  __syncthreads();
+  const int ts = block_inclusive_scan(ns, sh) - ns;
+  __syncthreads();
+  const int total_s = sh[16];
+  if (e < E) write_expert_tiles(e, excl, c, plan, nb, ns, tb, ts, tiles, small_tiles);
+  if (threadIdx.x == 0) {
+    *tiles.count = min(total, tiles.cap);
+    if (small_tiles.cap > 0) *small_tiles.count = min(total_s, small_tiles.cap);
   }
-  if (threadIdx.x == 0) *tiles.count = min(total, tiles.cap);
 }
 
 // Position of an assignment whose rank inside its expert's stable order is r: the kept rows
@@ -244,8 +279,8 @@ constexpr int kSmallTokens = 1024;
 __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ idx, int64_t T, int k,
                                                              int E, int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                             int32_t* __restrict__ inv, TileList tiles, int bm,
-                                                             int capacity) {
+                                                             int32_t* __restrict__ inv, TileList tiles,
+                                                             TileList small_tiles, TilePlan plan, int capacity) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* bits = reinterpret_cast<uint64_t*>(smem);  // [4][E]
   int32_t* pre = reinterpret_cast<int32_t*>(bits + 4 * E);  // [4][E]
@@ -254,8 +289,10 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   int32_t* doff = off + E + 1;                          // [E + 1] offsets of the dropped counts
   int32_t* kc = pre;                                    // [E] kept counts (pass 1 only)
   int32_t* dc = pre + E;                                // [E] dropped counts (pass 1 only)
-  int32_t* mt = pre + 2 * E;                            // [E] M-tiles per expert (pass 1 only)
-  int32_t* tb = pre;                                    // [E + 1] first tile of each expert (pass 1)
+  int32_t* mt = pre + 2 * E;                            // [E] main-list tiles per expert (pass 1 only)
+  int32_t* ms = pre + 3 * E;                            // [E] remainder-list tiles per expert (pass 1)
+  int32_t* tb = pre;                                    // [E + 1] first main-list tile (pass 1)
+  int32_t* ts = reinterpret_cast<int32_t*>(bits);       // [E + 1] first remainder tile (pass 1; bits is free)
   __shared__ int sh[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t A = T * k;
@@ -279,24 +316,24 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   for (int e = tid; e < E; e += 256) {
     counts[e] = run[e];
     offsets[e] = off[e];
-    mt[e] = (off[e + 1] - off[e] + bm - 1) / bm;
+    int nb, ns;
+    expert_tile_counts(off[e + 1] - off[e], plan, nb, ns);
+    mt[e] = nb;
+    ms[e] = ns;
   }
   if (tid == 0) offsets[E] = off[E];
   __syncthreads();
   if (tiles.cap > 0) {
     block_exclusive_scan_e(mt, E, tb, sh);
     __syncthreads();
-    for (int e = tid; e < E; e += 256) {
-      const int c = off[e + 1] - off[e];
-      for (int i = 0; i < mt[e]; ++i) {
-        const int ti = tb[e] + i;
-        if (ti >= tiles.cap) break;
-        tiles.expert[ti] = e;
-        tiles.row0[ti] = off[e] + i * bm;
-        tiles.rows[ti] = min(bm, c - i * bm);
-      }
+    block_exclusive_scan_e(ms, E, ts, sh);
+    __syncthreads();
+    for (int e = tid; e < E; e += 256)
+      write_expert_tiles(e, off[e], off[e + 1] - off[e], plan, mt[e], ms[e], tb[e], ts[e], tiles, small_tiles);
+    if (tid == 0) {
+      *tiles.count = min(tb[E], tiles.cap);
+      if (small_tiles.cap > 0) *small_tiles.count = min(ts[E], small_tiles.cap);
     }
-    if (tid == 0) *tiles.count = min(tb[E], tiles.cap);
     __syncthreads();
   }
   for (int e = tid; e < E; e += 256) run[e] = 0;
@@ -353,7 +390,7 @@ size_t dispatch_scratch_bytes(const Layer& ly) {
 
 hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
-                           int bm, hipStream_t s) {
+                           const TileList& small_tiles, const TilePlan& plan, hipStream_t s) {
   if (ly.T <= 0) return hipSuccess;
   const int cap = static_cast<int>(ly.capacity);  // <= T rounded up to 8, below 2^31
   if (ly.T <= kSmallTokens) {
@@ -362,7 +399,7 @@ hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts,
     const size_t lds = static_cast<size_t>(ly.E) * 4 * (sizeof(uint64_t) + sizeof(int32_t)) +
                        static_cast<size_t>(3 * ly.E + 2) * sizeof(int32_t);
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), lds, s, idx, ly.T, ly.k, ly.E, counts, offsets,
-                       perm, inv, tiles, bm, cap);
+                       perm, inv, tiles, small_tiles, plan, cap);
     return hipGetLastError();
   }
   const int nblk = num_rank_blocks(ly.T);
@@ -375,7 +412,7 @@ hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts,
                      blk);
   hipLaunchKernelGGL(scan_cols_kernel, dim3(ly.E), dim3(256), 0, s, blk, nblk, counts);
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, counts, nullptr, offsets, ly.E,
-                     bm, tiles, cap, drop_off);
+                     plan, tiles, small_tiles, cap, drop_off);
   hipLaunchKernelGGL(permute_kernel, dim3(static_cast<unsigned>((A + 255) / 256)), dim3(256), 0, s,
                      idx, rank, blk, nblk, offsets, A, ly.k, ly.E, perm, inv, cap, drop_off);
   return hipGetLastError();
@@ -394,9 +431,9 @@ hipError_t launch_zero_dropped(const Layer& ly, const int32_t* offsets, const in
 }
 
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
-                              int bm, hipStream_t s) {
+                              const TileList& small_tiles, const TilePlan& plan, hipStream_t s) {
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, nullptr, offsets, nullptr,
-                     ly.E, bm, tiles, 0, nullptr);
+                     ly.E, plan, tiles, small_tiles, 0, nullptr);
   return hipGetLastError();
 }
 
