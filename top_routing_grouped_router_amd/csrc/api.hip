@@ -346,7 +346,11 @@ hipError_t run_experts_mx(const Layer& ly, const void* z, const int32_t* perm, c
   g1.b_scale = w->w1_mx_scale;
   g1.b_scale_ld = ly.K / 32;
   g1.b_scale_group_stride = 2 * ly.h * (ly.K / 32);
+  // the activation leaves GEMM1's epilogue already MX-quantised (codes + block scales); the
+  // bf16 activation is never stored
   g1.C = act;
+  g1.c_codes = mb.aq;
+  g1.c_scales = mb.as;
   g1.ldc = ly.h;
   g1.N = ly.h;
   g1.Kd = ly.K;
@@ -356,7 +360,6 @@ hipError_t run_experts_mx(const Layer& ly, const void* z, const int32_t* perm, c
   g1.c_rows = A;
   g1.rows_bound = A;
   if ((e = launch_gemm_mx(g1, s)) != hipSuccess) return e;
-  if ((e = launch_mx_quantize(act, A, ly.h, mb.aq, mb.as, s)) != hipSuccess) return e;
   GemmCall g2{};
   g2.A = mb.aq;
   g2.lda = ly.h;

@@ -35,6 +35,27 @@ template <> struct Elem<uint16_t> {
   __device__ static void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
 };
 
+// ---------------------------------------------------------------- MXFP8 (OCP microscaling)
+
+// E8M0 scale code of a 32-element block with absolute maximum amax: floor(log2 amax) - 8 + 127,
+// clamped to [0, 254]; 0 for an all-zero block.
+__device__ __forceinline__ int mx_scale_code(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int ex;
+  frexpf(amax, &ex);  // amax = m * 2^ex with m in [0.5, 1): floor(log2 amax) = ex - 1
+  return min(max(ex - 1 - 8 + 127, 0), 254);
+}
+
+// Four values, already divided by the block scale, as E4M3 codes in one word (first value in
+// byte 0). v_cvt_pk_fp8_f32 rounds to nearest-even and returns NaN above 464, so the values are
+// clamped to the largest code, 448, first: the saturating rounding.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  const auto cl = [](float v) { return fminf(fmaxf(v, -448.f), 448.f); };
+  uint32_t r = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false));
+  r = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), static_cast<int>(r), true));
+  return r;
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -209,6 +230,10 @@ struct GemmCall {
   const uint8_t* b_scale;
   int64_t b_scale_ld;
   int64_t b_scale_group_stride;  // scale bytes between consecutive experts' weights
+  // MXFP8 output of the SwiGLU GEMM: E4M3 codes (c_rows, ldc) and block scales (c_rows, N / 32)
+  // instead of C
+  uint8_t* c_codes;
+  uint8_t* c_scales;
   // Bounds used to clamp every row index a kernel derives from device data, so that a
   // corrupt index can never address memory outside the operands.
   int64_t a_rows;           // rows of A

@@ -168,7 +168,7 @@ __device__ __forceinline__ void sched_stage() {
   sched_stage_step<0, KSTEPS, KREADS, KMFMA, KLOADS, KLOADS>();
 }
 
-template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false>
+template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false, bool OUT_MX = false>
 __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
   static_assert(S::NSTAGE == 2, "the persistent loop runs a two-slot ring");
   static_assert(!SWIGLU || S::TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
@@ -473,8 +473,33 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         const int lr = k * RPI + tid / CPR;
         const int m = tile_row(rho, lr);
         const int64_t orow = SCATTER ? static_cast<int64_t>(sidx[SCATTER ? k : 0]) : t.row0 + m;
-        if (m < t.rows && col < c.N)
-          *reinterpret_cast<u32x4_t*>(Cbase + min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col) = v[k];
+        if constexpr (OUT_MX) {
+          // MXFP8 output (the bf16 values staged above, quantised as the standalone quantiser
+          // does): a 32-column block is the 16-byte chunks of 4 adjacent lanes of one row;
+          // its amax comes from two lane exchanges inside the group, executed by every lane.
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(v[k][i] << 16);
+            x[2 * i + 1] = __uint_as_float(v[k][i] & 0xFFFF0000u);
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+          amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+          const int sc = mx_scale_code(amax), sh = 127 - sc;
+          const uint32_t q0 = pack4_e4m3(ldexpf(x[0], sh), ldexpf(x[1], sh), ldexpf(x[2], sh), ldexpf(x[3], sh));
+          const uint32_t q1 = pack4_e4m3(ldexpf(x[4], sh), ldexpf(x[5], sh), ldexpf(x[6], sh), ldexpf(x[7], sh));
+          if (m < t.rows && col < c.N) {
+            const int64_t r = min(max(orow, int64_t(0)), c.c_rows - 1);
+            *reinterpret_cast<uint2*>(c.c_codes + r * c.ldc + col) = make_uint2(q0, q1);
+            if ((cc & 3) == 0) c.c_scales[r * (c.N / 32) + col / 32] = static_cast<uint8_t>(sc);
+          }
+        } else {
+          if (m < t.rows && col < c.N)
+            *reinterpret_cast<u32x4_t*>(Cbase + min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col) = v[k];
+        }
       }
     }
   };
@@ -606,6 +631,19 @@ int gemm_mx_tile_m() { return ShapeLargeMX::BM; }
 
 hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s) {
   if (c.dense_M > 0 || c.Kd % ShapeLargeMX::BK != 0 || !c.a_scale || !c.b_scale) return hipErrorInvalidValue;
+  if (c.c_codes) {
+    // SwiGLU GEMM with an MXFP8 output (codes + block scales; N a multiple of 32)
+    if (c.swiglu_h <= 0 || !c.gather || c.scatter || !c.c_scales || c.N % 32 != 0) return hipErrorInvalidValue;
+    using S = ShapeLargeMX;
+    const int64_t ntn = (c.N + S::BN / 2 - 1) / (S::BN / 2);
+    const int64_t upper = static_cast<int64_t>(c.tiles.cap) * ntn;
+    if (upper <= 0 || c.rows_bound <= 0) return hipSuccess;
+    int64_t grid = std::min<int64_t>(upper, static_cast<int64_t>(device_cu_count()) * S::WG_PER_CU);
+    grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+    hipLaunchKernelGGL((gemm_bf16_kernel<S, true, true, false, false, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(S::NT), 0, s, c);
+    return hipGetLastError();
+  }
   return launch_shape<ShapeLargeMX>(c, s, ShapeLargeMX::WG_PER_CU);
 }
 

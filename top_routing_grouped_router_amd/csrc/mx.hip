@@ -22,13 +22,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  const auto cl = [](float v) { return fminf(fmaxf(v, -448.f), 448.f); };
-  uint32_t r = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false));
-  r = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), static_cast<int>(r), true));
-  return r;
-}
-
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t nb = cols / 32;
@@ -49,12 +42,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __rest
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int s = 0;
-  if (amax > 0.f) {
-    int ex;
-    frexpf(amax, &ex);                 // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
-    s = min(max(ex - 1 - 8 + 127, 0), 254);
-  }
+  const int s = mx_scale_code(amax);
   const int sh = 127 - s;              // multiply by 2^sh: exact
   uint32_t out[8];
 #pragma unroll
