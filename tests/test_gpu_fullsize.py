@@ -15,8 +15,8 @@ import torch
 
 import workloads
 from oracle import moe_oracle as O
-from parity import (assert_close, assert_weights_close, check_routing_invariants, flip_allowance,
-                    np32, oracle_inputs, routing_matches, sample_tokens)
+from parity import (assert_close, assert_weights_close, bf16_spacing, check_routing_invariants, flip_allowance,
+                    mx_expert_allowance, np32, oracle_inputs, routing_matches, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +67,39 @@ def test_full_size_layer(name):
                  None if fa is None else fa[same])
     print(f"  gpu {t1 - t0:.1f}s oracle+checks {time.time() - t1:.1f}s, {int(same.sum())}/{len(sample)} tokens compared",
           flush=True)
+
+
+@pytest.mark.parametrize("name", [n for n in workloads.CONFIG_ORDER if n != "tiny_f32"])
+def test_full_size_layer_mxfp8(name):
+    """The same full-size check with the expert matmuls in MXFP8. MX quantisation is per token
+    row (z, activation) and per weight row, so the oracle on a sample of tokens is again the
+    full layer on those rows."""
+    print(f"[case] full-size mxfp8 {name}", flush=True)
+    cfg, w, x = workloads.make_workload(name, device="cuda", expert_precision="mxfp8")
+    T = x.shape[0]
+    layer = moe.MoELayer(cfg, w)
+    y, r = layer(x, routing=True)
+    torch.cuda.synchronize()
+    check_routing_invariants(cfg, r, T)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    sample = sample_tokens(T, 64 if T > 64 else T, seed=2)
+    xs = np32(x[torch.from_numpy(sample).cuda()])
+    logits = O.router_logits(xs, np32(w["router_weight"]), np32(w["router_bias"]))
+    pre = O.route(cfgO, logits, np32(w["score_bias"]))
+    wo = oracle_inputs(w, np.unique(pre["idx"]))
+    ref = O.forward(cfgO, wo, xs)
+    gi = r["expert_indices"].cpu().numpy()[sample]
+    key_tol = 1e-4 * max(1.0, float(np.abs(ref["keys"]).max()))
+    same = routing_matches(cfgO, gi, ref, key_tol)
+    assert same.mean() >= 0.97, same.mean()
+    allow = None
+    if not cfgO.latent_dim:
+        a = mx_expert_allowance(cfgO, ref, wo) + bf16_spacing(ref["Y"])
+        n = len(sample)
+        allow = (np.abs(ref["w"])[:, :, None] * a[np.asarray(ref["inv"]).reshape(n, -1)]).sum(axis=1)[same]
+    ys = np32(y)[sample]
+    d = np.abs(ys[same] - ref["y"][same])
+    print(f"  max-abs {d.max():.3e} rel-fro {np.linalg.norm(ys[same] - ref['y'][same]) / np.linalg.norm(ref['y'][same]):.3e}",
+          flush=True)
+    assert_close(ys[same], ref["y"][same], "bf16", f"full-size mxfp8 {name}", allow,
+                 budget_share=None if allow is None else 1.0)
