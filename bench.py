@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mxfp8", action="store_true",
+                    help="skip the extra measurement of the same layer with MXFP8 expert matmuls")
     ap.add_argument("--stages", action="store_true", help="also time each stage call alone")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference the HBM "
@@ -122,12 +124,20 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
         return None
 
     def per_kernel(folder):
-        out = {"gemm1": [], "gemm2": []}
+        # one stage launch runs each GEMM as up to two kernels (the large tile shape and the
+        # small one for remainder rows): average each kernel over its dispatches, then add the
+        # kernels of a GEMM
+        by_name = {}
         for name, v in _counter_rows(folder):
             kind = gemm_kind(name)
             if kind:
-                out[kind].append(v)
-        return {k: _mean(v) for k, v in out.items()}
+                by_name.setdefault((kind, name), []).append(v)
+        out = {"gemm1": 0.0, "gemm2": 0.0}
+        for (kind, _), vals in by_name.items():
+            out[kind] += _mean(vals)
+        if not out["gemm1"] or not out["gemm2"]:
+            raise SystemExit("counter record: expert GEMM kernels not found in the profile")
+        return out
 
     def copy_kib(folder):
         vals = sorted((v for name, v in _counter_rows(folder) if "copyBuffer" in name), reverse=True)
@@ -258,6 +268,28 @@ def main():
                      "traffic": recorded_traffic(name) if args.precision == "bf16" else None,
                      "stage_ms": round(gemm_ms, 4), "flops_per_launch": gemm_flops},
     }
+    if args.precision == "bf16" and cfg["dtype"] == "bf16" and not args.no_mxfp8:
+        # The same layer with the expert matmuls in MXFP8 (block-scaled E4M3; weights quantised
+        # once, outside the timed region): an extra record, not the headline.
+        cfg8 = dict(cfg, expert_precision="mxfp8")
+        layer8 = moe.MoELayer(cfg8, w)
+        for _ in range(args.warmup):
+            layer8(x, out=y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer8(x, out=y)
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t0) * 1e3 / args.steps
+        w8 = layer8.weights
+        for _ in range(2):
+            moe.experts_forward(cfg8, w8, z, offs, perm)
+        g8 = event_time_ms(lambda: moe.experts_forward(cfg8, w8, z, offs, perm), max(args.steps, 5), torch)
+        a8 = gemm_flops / (g8 / 1e3) / 1e12
+        out["mxfp8_experts"] = {"value": round(T / (ms8 / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms8, 4),
+                                "stage_ms": round(g8, 4), "achieved_tflops": round(a8, 1),
+                                "peak_tflops": PEAK_FP8_TFLOPS, "frac": round(a8 / PEAK_FP8_TFLOPS, 4)}
+        del layer8, w8
     if args.stages:
         st = {}
         st["router"] = event_time_ms(lambda: moe.router_forward(cfg, w, x, logits=False, scores=False), 5, torch)
