@@ -1,4 +1,6 @@
-"""Plain CPU oracle of the routed Mixture-of-Experts layer forward pass.
+"""Plain CPU oracle of the routed Mixture-of-Experts layer: the forward pass and the backward
+of the routed experts (SwiGLU backward, the grouped matmuls' input and weight gradients, the
+combine backward).
 
 TEST INFRASTRUCTURE. Only the tests, the smoke check of the package entry file and the
 bench's cpu_baseline leg may import or call this module. The HIP path never does, and this
@@ -37,6 +39,17 @@ is 0), capacity = 8 * ceil(capacity_factor * top_k * T / (8 * E)).
 
 Balancing state ([OC3 "Счётчики и bias-корректировка"]): the count accumulator, the load
 imbalance metric max/mean, and the score_bias update by bias_gamma * sign(ideal - actual).
+
+Backward ([OC3 "SwiGLU с квантизацией"]: the activation keeps its input H, the backward
+splits it into up and gate and forms sigmoid, silu, its derivative and the two gradients in
+fp32 or better, concatenated in the storage dtype; [OC3 "Вычисления экспертов и точность"]:
+each expert's gradients come from its own rows of the grouped matmuls). Readings: H is saved
+in the layer dtype; d_act, dH, the per-copy input gradients and the weight gradients are
+stored in the layer dtype; a token's k copies are summed in float64 and rounded once.
+
+Pins of the backward (tests/test_oracle_backward_pins.py): hand-worked cases, torch autograd
+of an independent dense per-assignment forward, central finite differences of the oracle's
+own forward, and bf16 representability of every stored gradient.
 
 Pins (tests/test_oracle_pins.py): parameter counts against the element counts of the
 generated tensors and the golden table; logits against an exactly-rounded fsum dot
@@ -501,6 +514,123 @@ def forward(cfg: MoEConfig, weights: dict, x) -> dict:
     out["o"] = o
     out.update(restore_routed_output(cfg, o, weights.get("norm_weight"), weights.get("up_proj")))
     return out
+
+
+# ------------------------------------------------------------------- backward (experts)
+
+def expert_mlp_train(cfg: MoEConfig, z_rows, w1_e, w2_e) -> dict:
+    """One expert's SwiGLU MLP as the training forward runs it: the same H, act and Y as
+    expert_mlp, plus what the backward reads. [OC3 "SwiGLU с квантизацией"]: the activation
+    function keeps its input for the backward when that input needs a gradient; that input is
+    H, stored in the layer dtype like every tensor that leaves a matmul here. act is computed
+    from the unrounded H, as in the inference forward, and stored in the layer dtype."""
+    h = cfg.hidden_size
+    H = _f64(z_rows) @ _f64(w1_e).T
+    up, gate = H[:, :h], H[:, h:]
+    with np.errstate(over="ignore"):
+        act = round_to(up * gate / (1.0 + np.exp(-gate)), cfg.dtype)
+    Y = round_to(act @ _f64(w2_e).T, cfg.dtype)
+    return dict(H=round_to(H, cfg.dtype), act=act, Y=Y)
+
+
+def run_experts_train(cfg: MoEConfig, z, idx, w1, w2, capacity: Optional[int] = None) -> dict:
+    """run_experts with the saved tensors of the training forward: H (A, 2h) and act (A, h)
+    in sorted order, rows of dropped assignments 0."""
+    k = cfg.top_k
+    counts = expert_counts(idx, cfg.num_experts)
+    kept_counts = counts if capacity is None else np.minimum(counts, capacity)
+    offsets = expert_offsets(kept_counts)
+    perm, inv, kept = capacity_permutation(idx, cfg.num_experts, capacity)
+    z_perm = _f64(z)[perm // k]
+    A, h = perm.size, cfg.hidden_size
+    Y = np.zeros((A, z_perm.shape[1]))
+    H = np.zeros((A, 2 * h))
+    act = np.zeros((A, h))
+    for e in np.nonzero(kept_counts)[0]:
+        rows = slice(offsets[e], offsets[e + 1])
+        r = expert_mlp_train(cfg, z_perm[rows], w1[e], w2[e])
+        H[rows], act[rows], Y[rows] = r["H"], r["act"], r["Y"]
+    return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, kept=kept, z_perm=z_perm,
+                H=H, act=act, Y=Y)
+
+
+def swiglu_backward(cfg: MoEConfig, H, d_act) -> np.ndarray:
+    """[OC3 "SwiGLU с квантизацией"], the plain backward: the last dimension of the saved
+    input splits in halves, up then gate; sigmoid(gate), silu = gate * sigmoid(gate), its
+    derivative sigmoid(gate) * (1 + gate * (1 - sigmoid(gate))) and the two gradients
+    d_up = d_act * silu and d_gate = d_act * up * silu' are formed in fp32 or better (float64
+    here) and concatenated back, [d_up | d_gate], in the layer dtype."""
+    h = cfg.hidden_size
+    H = _f64(H)
+    up, gate = H[:, :h], H[:, h:]
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-gate))
+    silu = gate * sig
+    dsilu = sig * (1.0 + gate * (1.0 - sig))
+    d_act = _f64(d_act)
+    return round_to(np.concatenate([d_act * silu, d_act * up * dsilu], axis=1), cfg.dtype)
+
+
+def experts_backward(cfg: MoEConfig, z, idx, w1, w2, saved: dict, dY_assign,
+                     capacity: Optional[int] = None) -> dict:
+    """Gradients of the routed experts stage: the input of the stage is z (T, K) and its
+    output the per-assignment rows Y (A, K) in assignment order t*k+j; given dY_assign (the
+    gradient of those rows) this returns dz (T, K), dw1 (E, 2h, K) and dw2 (E, K, h).
+
+    [OC3 "Вычисления экспертов и точность"]: each expert's rows go through a grouped matmul,
+    so each expert's gradients come from its own rows only. Per expert e on its kept rows R
+    (sorted order), with the saved H and act of the training forward:
+      d_act   = dY[R] @ w2[e]            (the grad of act @ w2[e]^T), stored in the layer dtype;
+      dH      = swiglu_backward(H[R], d_act)   ([OC3 "SwiGLU с квантизацией"]);
+      dz_perm = dH @ w1[e]               (the grad of z_perm @ w1[e]^T), layer dtype;
+      dw2[e]  = dY[R]^T @ act[R],  dw1[e] = dH^T @ z_perm[R], layer dtype (0 without rows).
+    [OC3 "Пересылка токенов между экспертами"]: z_perm is z gathered by perm // k, so the
+    gradient of z sums its k copies: dz[t] = sum_j dz_perm[inv[t*k+j]], summed in float64 and
+    stored once in the layer dtype (reading: one rounding after the sum). Dropped assignments
+    ([OC3 "Ёмкость эксперта и переполнение"]) produced 0 and pass no gradient."""
+    k = cfg.top_k
+    E, h = cfg.num_experts, cfg.hidden_size
+    counts = expert_counts(idx, E)
+    kept_counts = counts if capacity is None else np.minimum(counts, capacity)
+    offsets = expert_offsets(kept_counts)
+    perm, inv, kept = capacity_permutation(idx, E, capacity)
+    z = _f64(z)
+    T, K = z.shape
+    z_perm = z[perm // k]
+    dY = _f64(dY_assign)[perm]          # sorted order
+    dz_perm = np.zeros((perm.size, K))
+    dH_all = np.zeros((perm.size, 2 * h))
+    dw1 = np.zeros((E, 2 * h, K))
+    dw2 = np.zeros((E, K, h))
+    for e in np.nonzero(kept_counts)[0]:
+        R = slice(offsets[e], offsets[e + 1])
+        d_act = round_to(dY[R] @ _f64(w2[e]), cfg.dtype)
+        dH = swiglu_backward(cfg, saved["H"][R], d_act)
+        dH_all[R] = dH
+        dz_perm[R] = round_to(dH @ _f64(w1[e]), cfg.dtype)
+        dw2[e] = round_to(dY[R].T @ _f64(saved["act"][R]), cfg.dtype)
+        dw1[e] = round_to(dH.T @ z_perm[R], cfg.dtype)
+    dz = np.zeros((T, K))
+    inv2 = np.asarray(inv).reshape(T, k)
+    for j in range(k):
+        dz += dz_perm[inv2[:, j]]
+    return dict(dz=round_to(dz, cfg.dtype), dw1=dw1, dw2=dw2, dH=dH_all, dz_perm=dz_perm,
+                offsets=offsets, perm=perm, inv=inv)
+
+
+def combine_backward(cfg: MoEConfig, Y_assign, w, d_o) -> dict:
+    """Gradients of the weighted combine o[t] = sum_j w[t,j] * Y[t*k+j] ([OC3 "Пересылка
+    токенов между экспертами"]) with Y in assignment order: dY[t*k+j] = w[t,j] * d_o[t],
+    stored in the layer dtype (Y's), and dw[t,j] = sum_c d_o[t,c] * Y[t*k+j, c], rounded
+    to fp32 (the routing weights are fp32)."""
+    k = cfg.top_k
+    w = _f64(w)
+    T = w.shape[0]
+    d_o = _f64(d_o)
+    Y = _f64(Y_assign).reshape(T, k, -1)
+    dY = round_to(w[:, :, None] * d_o[:, None, :], cfg.dtype).reshape(T * k, -1)
+    dw = round_f32(np.einsum("tc,tjc->tj", d_o, Y))
+    return dict(dY=dY, dw=dw)
 
 
 # ------------------------------------------------------------------- balancing state

@@ -193,3 +193,80 @@ def test_planted_mx_mistake_is_caught(monkeypatch, target, bad, pin):
     monkeypatch.setattr(O, target, bad)
     with pytest.raises(AssertionError):
         pin()
+
+
+# ------------------------------------------------------------------ backward of the experts
+import test_oracle_backward_pins as B  # noqa: E402
+
+_orig_experts_backward = O.experts_backward
+
+
+def _swiglu_bwd_halves_swapped(cfg, H, d_act):
+    h = cfg.hidden_size
+    H = np.asarray(H, np.float64)
+    up, gate = H[:, :h], H[:, h:]
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    d_act = np.asarray(d_act, np.float64)
+    # gate gradient first
+    return O.round_to(np.concatenate([d_act * up * sig * (1 + gate * (1 - sig)), d_act * gate * sig], 1),
+                      cfg.dtype)
+
+
+def _swiglu_bwd_sigmoid_as_derivative(cfg, H, d_act):
+    h = cfg.hidden_size
+    H = np.asarray(H, np.float64)
+    up, gate = H[:, :h], H[:, h:]
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    d_act = np.asarray(d_act, np.float64)
+    # silu' taken as sigmoid alone (the gate * sigmoid * (1 - sigmoid) term dropped)
+    return O.round_to(np.concatenate([d_act * gate * sig, d_act * up * sig], 1), cfg.dtype)
+
+
+def _dz_from_first_copy_only(cfg, z, idx, w1, w2, saved, dY_assign, capacity=None):
+    g = _orig_experts_backward(cfg, z, idx, w1, w2, saved, dY_assign, capacity)
+    T = np.asarray(z).shape[0]
+    first = np.asarray(g["inv"]).reshape(T, cfg.top_k)[:, 0]
+    g["dz"] = O.round_to(g["dz_perm"][first], cfg.dtype)  # copies not summed
+    return g
+
+
+def _dw2_with_act_in_assignment_order(cfg, z, idx, w1, w2, saved, dY_assign, capacity=None):
+    g = _orig_experts_backward(cfg, z, idx, w1, w2, saved, dY_assign, capacity)
+    perm, offsets = g["perm"], g["offsets"]
+    act_assign = np.asarray(saved["act"])[np.asarray(g["inv"])]  # sorted rows read in assignment order
+    dY = np.asarray(dY_assign, np.float64)[perm]
+    for e in range(cfg.num_experts):
+        R = slice(offsets[e], offsets[e + 1])
+        if offsets[e + 1] > offsets[e]:
+            g["dw2"][e] = O.round_to(dY[R].T @ act_assign[R], cfg.dtype)
+    return g
+
+
+def _combine_bwd_without_weight(cfg, Y_assign, w, d_o):
+    k = cfg.top_k
+    d_o = np.asarray(d_o, np.float64)
+    T = d_o.shape[0]
+    Y = np.asarray(Y_assign, np.float64).reshape(T, k, -1)
+    dY = O.round_to(np.repeat(d_o[:, None, :], k, axis=1), cfg.dtype).reshape(T * k, -1)  # w dropped
+    return dict(dY=dY, dw=O.round_f32(np.einsum("tc,tjc->tj", d_o, Y)))
+
+
+_DENSE_K2 = dict(d_model=32, num_experts=5, top_k=2, hidden_size=16)
+
+BACKWARD_MUTATIONS = [
+    ("swiglu_backward", _swiglu_bwd_halves_swapped, lambda: B.test_swiglu_backward_matches_torch_autograd()),
+    ("swiglu_backward", _swiglu_bwd_sigmoid_as_derivative, lambda: B.test_swiglu_backward_closed_forms_at_limits()),
+    ("experts_backward", _dz_from_first_copy_only,
+     lambda: B.test_experts_backward_matches_autograd_of_dense_forward(_DENSE_K2)),
+    ("experts_backward", _dw2_with_act_in_assignment_order,
+     lambda: B.test_experts_backward_matches_autograd_of_dense_forward(_DENSE_K2)),
+    ("combine_backward", _combine_bwd_without_weight, lambda: B.test_combine_backward_matches_autograd()),
+]
+
+
+@pytest.mark.parametrize("target,bad,pin", BACKWARD_MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in BACKWARD_MUTATIONS])
+def test_planted_backward_mistake_is_caught(monkeypatch, target, bad, pin):
+    monkeypatch.setattr(O, target, bad)
+    with pytest.raises(AssertionError):
+        pin()
