@@ -1,5 +1,6 @@
 /*
- * moe_mi355x.h -- C ABI of the routed Mixture-of-Experts layer forward pass on MI355X (gfx950).
+ * moe_mi355x.h -- C ABI of the routed Mixture-of-Experts layer on MI355X (gfx950): the forward
+ * pass, and the backward of the routed experts and of the combine.
  *
  * What the layer computes is defined on the page "Как устроен Olmo-core 3: обучение больших
  * MoE-моделей" (cited below as [OC3 "<section title>"]):
@@ -46,7 +47,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
 
@@ -298,6 +299,66 @@ MOE_API moe_status_t moe_combine(const moe_config_t* cfg, const moe_weights_t* w
 MOE_API moe_status_t moe_latent_up(const moe_config_t* cfg, const moe_weights_t* weights,
                            int64_t num_tokens, const void* n, void* y, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* ------------------------------------------------------------------------ backward */
+
+/*
+ * Training forward of the routed experts: what moe_experts_forward computes (same arguments,
+ * same y_assign), plus the two tensors the backward reads ([OC3 "SwiGLU с квантизацией"]: the
+ * activation keeps its input for the backward), both in sorted order:
+ *   h_saved (A, 2h) D: the pre-activation H = z_t * w1[e]^T = [up | gate] of each kept row
+ *     p < expert_offsets[E], rounded to D (act is computed from the unrounded H);
+ *   act_saved (A, h) D: the SwiGLU activation of those rows.
+ * Rows p >= expert_offsets[E] of both are left unwritten. bf16 expert precision only
+ * (UNSUPPORTED with MXFP8). Uses the workspace (moe_workspace_size bytes).
+ */
+MOE_API moe_status_t moe_experts_forward_train(const moe_config_t* cfg, const moe_weights_t* weights,
+                                               int64_t num_tokens, const void* z, const int32_t* expert_offsets,
+                                               const int32_t* permutation, void* y_assign, void* h_saved,
+                                               void* act_saved, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace moe_experts_backward needs for T tokens: about (2 * K + 2h) * T *
+ * top_k elements of D (dY and z in sorted order, dH) plus the M-tile lists. UNSUPPORTED when
+ * the backward does not serve the configuration (see moe_experts_backward). */
+MOE_API moe_status_t moe_experts_backward_workspace_size(const moe_config_t* cfg, int64_t num_tokens,
+                                                         size_t* bytes);
+
+/*
+ * Backward of the routed experts ([OC3 "Вычисления экспертов и точность"]: each expert's
+ * gradients come from its own rows of the grouped products; [OC3 "SwiGLU с квантизацией"]: the
+ * SwiGLU backward; [OC3 "Пересылка токенов между экспертами"]: the gather by the permutation).
+ * Inputs: z (T, K) D, expert_offsets (E+1) and permutation (A) as given to the forward, the
+ * forward's h_saved and act_saved (moe_experts_forward_train), and dy_assign (A, K) D, the
+ * gradient of y_assign (assignment order t*k+j). With dY[p] = dy_assign[permutation[p]] and
+ * z_perm[p] = z[permutation[p] / k], for each expert e on its kept rows R:
+ *   d_act   = dY[R] * w2[e]                          fp32 accumulation, stored as D;
+ *   dH      = [d_act * silu(gate) | d_act * up * silu'(gate)], silu' = sigmoid * (1 + gate *
+ *             (1 - sigmoid)), in fp32 from the saved H, stored as D;
+ *   dz_perm = dH * w1[e]                             stored as D;
+ *   dw2[e]  = dY[R]^T * act[R],  dw1[e] = dH^T * z_perm[R]   fp32 accumulation, stored as D.
+ * Outputs: dz (T, K) D = the sum over j (fp32, j ascending) of dz_perm of assignment t*k+j,
+ * dropped assignments contributing nothing; dw1 (E, 2h, K) D and dw2 (E, K, h) D, zero for
+ * experts without rows. ws: moe_experts_backward_workspace_size bytes. bf16 expert precision
+ * only; bf16 layers need A * 2h < 2^31, fp32 layers A, K and 2h at most 65535 (UNSUPPORTED
+ * otherwise). With T = 0 only dw1 and dw2 are written (zeros) and the other pointers may be NULL.
+ */
+MOE_API moe_status_t moe_experts_backward(const moe_config_t* cfg, const moe_weights_t* weights,
+                                          int64_t num_tokens, const void* z, const int32_t* expert_offsets,
+                                          const int32_t* permutation, const void* h_saved, const void* act_saved,
+                                          const void* dy_assign, void* dz, void* dw1, void* dw2, void* ws,
+                                          size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the weighted combine o[t] = sum_j expert_weights[t,j] * y_assign[t*k+j]
+ * ([OC3 "Пересылка токенов между экспертами"]): given d_out (T, K) D, the gradient of o,
+ *   dy_assign (A, K) D        = expert_weights[t,j] * d_out[t], rounded to D;
+ *   d_expert_weights (T, k) f32 = sum_c d_out[t,c] * y_assign[t*k+j,c] (NULL: not wanted).
+ * UNSUPPORTED for a latent layer with the up-projection input norm (its backward is not
+ * built). No workspace.
+ */
+MOE_API moe_status_t moe_combine_backward(const moe_config_t* cfg, int64_t num_tokens, const void* y_assign,
+                                          const float* expert_weights, const void* d_out, void* dy_assign,
+                                          float* d_expert_weights, void* stream);
 
 /* ------------------------------------------------------------------------ MXFP8 */
 

@@ -30,7 +30,8 @@ def test_header_declares_the_abi():
                  "moe_config_default", "moe_config_validate", "moe_num_params",
                  "moe_workspace_size", "moe_status_string", "moe_last_error_message",
                  "moe_abi_version", "moe_accumulate_expert_counts", "moe_load_imbalance",
-                 "moe_score_bias_update", "moe_expert_capacity"):
+                 "moe_score_bias_update", "moe_expert_capacity", "moe_experts_forward_train",
+                 "moe_experts_backward", "moe_experts_backward_workspace_size", "moe_combine_backward"):
         assert name in syms
 
 
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_size():
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     c = moe._CConfig()
     assert moe._config_default(ctypes.byref(c)) == 0
     assert c.struct_size == ctypes.sizeof(moe._CConfig)
@@ -187,3 +188,51 @@ def test_capacity_factor_validation():
     for bad in (-1.0, float("nan"), float("inf")):
         with pytest.raises(moe.MoEError):
             moe.validate(dict(d_model=64, num_experts=4, top_k=2, hidden_size=64, capacity_factor=bad))
+
+
+def test_backward_entry_points_validate_before_any_gpu_call():
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    cfg = moe.MoEConfig.of(workloads.layer_config("olmoe"))
+    c = cfg.to_c()
+    w = moe._CWeights()
+    w.w1 = w.w2 = fake
+    T = 128
+    need = moe.experts_backward_workspace_size(cfg, T)
+    assert need > T * cfg.top_k * (2 * cfg.expert_dim + 2 * cfg.hidden_size) * 2
+    args = [fake] * 9  # z, offsets, perm, h, act, dy, dz, dw1, dw2
+    for i, name in enumerate(("z", "expert_offsets", "permutation", "h_saved", "act_saved", "dy_assign",
+                              "dz", "dw1", "dw2")):
+        bad = list(args)
+        bad[i] = None
+        assert moe._experts_backward(ctypes.byref(c), ctypes.byref(w), T, *bad, fake, need, None) == 1, name
+        assert name in moe._last_error().decode()
+    # short workspace
+    assert moe._experts_backward(ctypes.byref(c), ctypes.byref(w), T, *args, fake, need - 1, None) == 3
+    # missing expert weights
+    assert moe._experts_backward(ctypes.byref(c), ctypes.byref(moe._CWeights()), T, *args, fake, need, None) == 1
+    # MXFP8 training is not built
+    mx = moe.MoEConfig.of(dict(workloads.layer_config("olmoe"), expert_precision="mxfp8"))
+    with pytest.raises(moe.MoEError) as e:
+        moe.experts_backward_workspace_size(mx, T)
+    assert e.value.status == 2
+    cm = mx.to_c()
+    assert moe._experts_forward_train(ctypes.byref(cm), ctypes.byref(w), T, *([fake] * 6), fake, 1 << 40, None) == 2
+    # fp32 layers beyond the fp32 kernels' grid
+    big = dict(workloads.layer_config("tiny_f32"))
+    with pytest.raises(moe.MoEError):
+        moe.experts_backward_workspace_size(big, 70000)
+    # bf16 operands above 4 GiB
+    with pytest.raises(moe.MoEError):
+        moe.experts_backward_workspace_size(workloads.layer_config("skewed"), 65536)
+    # training forward needs both saved buffers
+    assert moe._experts_forward_train(ctypes.byref(c), ctypes.byref(w), T, fake, fake, fake, fake, None, fake,
+                                      fake, 1 << 40, None) == 1
+    assert "h_saved" in moe._last_error().decode()
+    # combine backward: pointers, and no backward through the latent norm
+    assert moe._combine_backward(ctypes.byref(c), T, fake, fake, None, fake, None, None) == 1
+    lat = moe.MoEConfig.of(workloads.layer_config("latent896")).to_c()
+    assert moe._combine_backward(ctypes.byref(lat), T, fake, fake, fake, fake, None, None) == 2
+    # T = 0: only the weight gradients, which must be given
+    assert moe._combine_backward(ctypes.byref(c), 0, None, None, None, None, None, None) == 0
+    assert moe._experts_backward(ctypes.byref(c), ctypes.byref(w), 0, *([None] * 7), None, None, None, 0,
+                                 None) == 1

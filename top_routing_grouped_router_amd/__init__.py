@@ -93,6 +93,14 @@ _experts_forward = _sig("moe_experts_forward", c_i32, _P(_CConfig), _P(_CWeights
 _combine = _sig("moe_combine", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp, c_vp)
 _latent_up = _sig("moe_latent_up", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp,
                   ctypes.c_size_t, c_vp)
+_experts_forward_train = _sig("moe_experts_forward_train", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp,
+                              c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp)
+_experts_backward_ws = _sig("moe_experts_backward_workspace_size", c_i32, _P(_CConfig), c_i64,
+                            _P(ctypes.c_size_t))
+_experts_backward = _sig("moe_experts_backward", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp, c_vp,
+                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp)
+_combine_backward = _sig("moe_combine_backward", c_i32, _P(_CConfig), c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                         c_vp)
 _mx_quantize = _sig("moe_mx_quantize", c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp)
 _accumulate_counts = _sig("moe_accumulate_expert_counts", c_i32, c_i32, c_vp, c_vp, c_vp)
 _load_imbalance = _sig("moe_load_imbalance", c_i32, c_i32, c_vp, c_vp, c_vp)
@@ -419,6 +427,85 @@ def latent_up(cfg, weights: dict, n: torch.Tensor) -> torch.Tensor:
     _check(_latent_up(ctypes.byref(c), ctypes.byref(cw), T, _ptr(n), _ptr(y), _ptr(ws), ws.numel(),
                       _stream()))
     return y
+
+
+# --------------------------------------------------------------------------- backward
+# Page "Как устроен Olmo-core 3: обучение больших MoE-моделей", sections "SwiGLU с квантизацией"
+# (the saved pre-activation and the SwiGLU backward), "Вычисления экспертов и точность" (per-
+# expert gradients of the grouped products) and "Пересылка токенов между экспертами".
+
+def experts_forward_train(cfg, weights: dict, z: torch.Tensor, expert_offsets: torch.Tensor,
+                          permutation: torch.Tensor) -> dict:
+    """experts_forward plus the saved pre-activation h (A, 2h) and activation act (A, h), sorted
+    order, for experts_backward."""
+    cfg = MoEConfig.of(cfg)
+    T, K = z.shape[0], cfg.expert_dim
+    A, h = T * cfg.top_k, cfg.hidden_size
+    _expect(z, (T, K), cfg.torch_dtype, "z")
+    _expect(expert_offsets, (cfg.num_experts + 1,), torch.int32, "expert_offsets")
+    _expect(permutation, (A,), torch.int32, "permutation")
+    y = torch.empty((A, K), dtype=cfg.torch_dtype, device=z.device)
+    hs = torch.empty((A, 2 * h), dtype=cfg.torch_dtype, device=z.device)
+    act = torch.empty((A, h), dtype=cfg.torch_dtype, device=z.device)
+    ws = torch.empty(max(workspace_size(cfg, T), 1), dtype=torch.uint8, device=z.device)
+    c, cw = cfg.to_c(), _c_weights(cfg, weights)
+    _check(_experts_forward_train(ctypes.byref(c), ctypes.byref(cw), T, _ptr(z), _ptr(expert_offsets),
+                                  _ptr(permutation), _ptr(y), _ptr(hs), _ptr(act), _ptr(ws), ws.numel(),
+                                  _stream()))
+    return {"y_assign": y, "h": hs, "act": act}
+
+
+def experts_backward_workspace_size(cfg, num_tokens: int) -> int:
+    c = MoEConfig.of(cfg).to_c()
+    n = ctypes.c_size_t(0)
+    _check(_experts_backward_ws(ctypes.byref(c), num_tokens, ctypes.byref(n)))
+    return int(n.value)
+
+
+def experts_backward(cfg, weights: dict, z: torch.Tensor, expert_offsets: torch.Tensor,
+                     permutation: torch.Tensor, saved: dict, dy_assign: torch.Tensor,
+                     workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """Gradients of the routed experts: dz (T, K), dw1 (E, 2h, K), dw2 (E, K, h), from the
+    gradient dy_assign (A, K) of y_assign and the saved tensors of experts_forward_train."""
+    cfg = MoEConfig.of(cfg)
+    T, K = z.shape[0], cfg.expert_dim
+    A, h, E = T * cfg.top_k, cfg.hidden_size, cfg.num_experts
+    dt = cfg.torch_dtype
+    _expect(z, (T, K), dt, "z")
+    _expect(expert_offsets, (E + 1,), torch.int32, "expert_offsets")
+    _expect(permutation, (A,), torch.int32, "permutation")
+    _expect(saved["h"], (A, 2 * h), dt, "saved h")
+    _expect(saved["act"], (A, h), dt, "saved act")
+    _expect(dy_assign, (A, K), dt, "dy_assign")
+    if out is None:
+        out = {"dz": torch.empty((T, K), dtype=dt, device=z.device),
+               "dw1": torch.empty((E, 2 * h, K), dtype=dt, device=z.device),
+               "dw2": torch.empty((E, K, h), dtype=dt, device=z.device)}
+    if workspace is None:
+        workspace = torch.empty(max(experts_backward_workspace_size(cfg, T), 1), dtype=torch.uint8,
+                                device=z.device)
+    c, cw = cfg.to_c(), _c_weights(cfg, weights)
+    _check(_experts_backward(ctypes.byref(c), ctypes.byref(cw), T, _ptr(z), _ptr(expert_offsets),
+                             _ptr(permutation), _ptr(saved["h"]), _ptr(saved["act"]), _ptr(dy_assign),
+                             _ptr(out["dz"]), _ptr(out["dw1"]), _ptr(out["dw2"]), _ptr(workspace),
+                             workspace.numel(), _stream()))
+    return out
+
+
+def combine_backward(cfg, y_assign: torch.Tensor, expert_weights: torch.Tensor, d_out: torch.Tensor,
+                     want_weight_grad: bool = True) -> dict:
+    """dY (A, K) = w * d_out per assignment and d_expert_weights (T, k) = <d_out[t], Y[t*k+j]>."""
+    cfg = MoEConfig.of(cfg)
+    T, K = expert_weights.shape[0], cfg.expert_dim
+    _expect(y_assign, (T * cfg.top_k, K), cfg.torch_dtype, "y_assign")
+    _expect(expert_weights, (T, cfg.top_k), torch.float32, "expert_weights")
+    _expect(d_out, (T, K), cfg.torch_dtype, "d_out")
+    dy = torch.empty((T * cfg.top_k, K), dtype=cfg.torch_dtype, device=y_assign.device)
+    dw = torch.empty((T, cfg.top_k), dtype=torch.float32, device=y_assign.device) if want_weight_grad else None
+    c = cfg.to_c()
+    _check(_combine_backward(ctypes.byref(c), T, _ptr(y_assign), _ptr(expert_weights), _ptr(d_out), _ptr(dy),
+                             _ptr(dw), _stream()))
+    return {"dy_assign": dy, "d_expert_weights": dw}
 
 
 # --------------------------------------------------------------------------- balancing state

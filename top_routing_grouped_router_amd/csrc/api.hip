@@ -383,10 +383,11 @@ hipError_t run_experts_mx(const Layer& ly, const void* z, const int32_t* perm, c
   return launch_gemm_mx(g2, s);
 }
 
+// h_out: training forward, GEMM1 also stores the pre-activation H (A, 2h) in sorted order.
 hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, const TileList& tiles,
                        const TileList& small_tiles, const moe_weights_t* w, void* act, void* yassign,
-                       const MxBuffers& mb, hipStream_t s) {
-  if (ly.mx) return run_experts_mx(ly, z, perm, tiles, w, act, yassign, mb, s);
+                       const MxBuffers& mb, hipStream_t s, void* h_out = nullptr) {
+  if (ly.mx) return h_out ? hipErrorInvalidValue : run_experts_mx(ly, z, perm, tiles, w, act, yassign, mb, s);
   const void* w1 = w->w1;
   const void* w2 = w->w2;
   const int64_t A = ly.T * ly.k;
@@ -403,6 +404,7 @@ hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, cons
   g1.N = ly.h;
   g1.Kd = ly.K;
   g1.swiglu_h = ly.h;
+  g1.h_out = h_out;
   g1.tiles = tiles;
   g1.a_rows = ly.T;
   g1.c_rows = A;
@@ -438,6 +440,190 @@ hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, cons
   }
   if ((e = launch_gemm_f32(g1, false, nullptr, s)) != hipSuccess) return e;
   return launch_gemm_f32(g2, false, nullptr, s);
+}
+
+// ------------------------------------------------------------------ backward of the experts
+
+// Workspace of moe_experts_backward: the M-tile lists of the input-gradient GEMMs, dY and z in
+// sorted order (the dY buffer later holds the per-assignment input gradients), dH, and one
+// row of zeros read by the weight-gradient GEMMs past a group's last row.
+struct BwdLayout {
+  size_t tcount, texpert, trow0, trows, scount, sexpert, srow0, srows, dy, zs, dh, zero, total;
+  int32_t tile_cap, small_cap;
+};
+constexpr size_t kZeroRowBytes = 512;
+
+BwdLayout bwd_layout(const Layer& ly) {
+  BwdLayout b{};
+  Carve c;
+  const size_t E = static_cast<size_t>(ly.E), A = static_cast<size_t>(ly.T) * ly.k;
+  const size_t es = elem_size(ly);
+  const TilePlan plan = tile_plan(ly);
+  b.tile_cap = static_cast<int32_t>((A + plan.bm - 1) / plan.bm + E);
+  b.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs)) : 0;
+  b.tcount = c.take(4);
+  b.texpert = c.take(static_cast<size_t>(b.tile_cap) * 4);
+  b.trow0 = c.take(static_cast<size_t>(b.tile_cap) * 4);
+  b.trows = c.take(static_cast<size_t>(b.tile_cap) * 4);
+  b.scount = c.take(4);
+  b.sexpert = c.take(static_cast<size_t>(b.small_cap) * 4);
+  b.srow0 = c.take(static_cast<size_t>(b.small_cap) * 4);
+  b.srows = c.take(static_cast<size_t>(b.small_cap) * 4);
+  b.dy = c.take(A * static_cast<size_t>(ly.K) * es);
+  b.zs = c.take(A * static_cast<size_t>(ly.K) * es);
+  b.dh = c.take(A * 2 * static_cast<size_t>(ly.h) * es);
+  b.zero = c.take(kZeroRowBytes);
+  b.total = c.off;
+  return b;
+}
+
+struct BwdArgs {
+  const void* z;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const void* h_saved;
+  const void* act_saved;
+  const void* dy_assign;
+  void* dz;
+  void* dw1;
+  void* dw2;
+};
+
+// dY, z -> sorted order; d_act = dY w2[e] with the SwiGLU backward in its epilogue -> dH;
+// dw2[e] = dY^T act; dz_assign = dH w1[e] scattered to assignment order; dw1[e] = dH^T z;
+// dz = sum of each token's k rows of dz_assign.
+hipError_t run_experts_backward(const Layer& ly, const moe_weights_t* w, const BwdArgs& a, void* ws,
+                                const BwdLayout& L, hipStream_t s) {
+  const int64_t A = ly.T * ly.k;
+  const size_t es = elem_size(ly);
+  TileList tiles{at<int32_t>(ws, L.tcount), at<int32_t>(ws, L.texpert), at<int32_t>(ws, L.trow0),
+                 at<int32_t>(ws, L.trows), L.tile_cap};
+  TileList small_tiles{at<int32_t>(ws, L.scount), at<int32_t>(ws, L.sexpert), at<int32_t>(ws, L.srow0),
+                       at<int32_t>(ws, L.srows), L.small_cap};
+  void* dy_sorted = at<void>(ws, L.dy);
+  void* z_sorted = at<void>(ws, L.zs);
+  void* dh = at<void>(ws, L.dh);
+  void* dz_assign = dy_sorted;  // reused once the two dY products are enqueued
+  const TilePlan plan = tile_plan(ly);
+  hipError_t e;
+  const int32_t* kept = a.offsets + ly.E;
+  if ((e = launch_build_tiles(ly, a.offsets, tiles, small_tiles, plan, s)) != hipSuccess) return e;
+  if ((e = launch_fill_zero(at<void>(ws, L.zero), kZeroRowBytes, s)) != hipSuccess) return e;
+  if ((e = launch_gather_rows(a.dy_assign, A, a.perm, 1, kept, A, ly.K * es, dy_sorted, s)) != hipSuccess) return e;
+  if ((e = launch_gather_rows(a.z, ly.T, a.perm, ly.k, kept, A, ly.K * es, z_sorted, s)) != hipSuccess) return e;
+
+  // input gradient of the activation, then the SwiGLU backward: dH (A, 2h)
+  GemmCall d2{};
+  d2.A = dy_sorted;
+  d2.lda = ly.K;
+  d2.B = w->w2;              // (K, h) per expert: contraction K rows, h columns
+  d2.ldb = ly.h;
+  d2.b_group_stride = ly.K * ly.h;
+  d2.trans = 2;
+  d2.C = dh;
+  d2.ldc = 2 * ly.h;
+  d2.N = ly.h;
+  d2.Kd = ly.K;
+  d2.bwd_h = ly.h;
+  d2.h_in = a.h_saved;
+  d2.tiles = tiles;
+  d2.a_rows = A;
+  d2.c_rows = A;
+  d2.rows_bound = A;
+  // weight gradient of w2: dw2[e] (K, h) = sum_p dY[p]^T act[p]
+  GemmCall g2{};
+  g2.A = dy_sorted;
+  g2.lda = ly.K;
+  g2.B = a.act_saved;
+  g2.ldb = ly.h;
+  g2.trans = 3;
+  g2.C = a.dw2;
+  g2.ldc = ly.h;
+  g2.N = ly.h;
+  g2.dense_M = ly.K;
+  g2.group_offsets = a.offsets;
+  g2.groups = ly.E;
+  g2.c_group_stride = ly.K * ly.h;
+  g2.zero_row = at<void>(ws, L.zero);
+  g2.a_rows = A;
+  g2.c_rows = ly.K;
+  g2.rows_bound = A;
+  // input gradient of z_perm: dz_assign = dH w1[e], scattered to assignment order
+  GemmCall d1{};
+  d1.A = dh;
+  d1.lda = 2 * ly.h;
+  d1.B = w->w1;              // (2h, K) per expert: contraction 2h rows, K columns
+  d1.ldb = ly.K;
+  d1.b_group_stride = 2 * ly.h * ly.K;
+  d1.trans = 2;
+  d1.C = dz_assign;
+  d1.ldc = ly.K;
+  d1.scatter = a.perm;
+  d1.N = ly.K;
+  d1.Kd = 2 * ly.h;
+  d1.tiles = tiles;
+  d1.a_rows = A;
+  d1.c_rows = A;
+  d1.rows_bound = A;
+  // weight gradient of w1: dw1[e] (2h, K) = sum_p dH[p]^T z[p]
+  GemmCall g1{};
+  g1.A = dh;
+  g1.lda = 2 * ly.h;
+  g1.B = z_sorted;
+  g1.ldb = ly.K;
+  g1.trans = 3;
+  g1.C = a.dw1;
+  g1.ldc = ly.K;
+  g1.N = ly.K;
+  g1.dense_M = 2 * ly.h;
+  g1.group_offsets = a.offsets;
+  g1.groups = ly.E;
+  g1.c_group_stride = 2 * ly.h * ly.K;
+  g1.zero_row = at<void>(ws, L.zero);
+  g1.a_rows = A;
+  g1.c_rows = 2 * ly.h;
+  g1.rows_bound = A;
+
+  if (ly.bf16) {
+    const bool run_main = !main_list_empty(ly, plan);
+    GemmCall d2s = d2, d1s = d1;
+    d2s.tiles = small_tiles;
+    d1s.tiles = small_tiles;
+    if (run_main && (e = launch_gemm_bf16_dgrad(d2, 0, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_dgrad(d2s, 1, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_wgrad(g2, s)) != hipSuccess) return e;
+    if (run_main && (e = launch_gemm_bf16_dgrad(d1, 0, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_dgrad(d1s, 1, s)) != hipSuccess) return e;
+    if ((e = launch_gemm_bf16_wgrad(g1, s)) != hipSuccess) return e;
+  } else {
+    // fp32 layers: per-element kernels, the expert of each row found from the offsets
+    d2.group_offsets = a.offsets;
+    d2.groups = ly.E;
+    d1.group_offsets = a.offsets;
+    d1.groups = ly.E;
+    if ((e = launch_dgrad_f32(d2, s)) != hipSuccess) return e;
+    if ((e = launch_wgrad_f32(g2, s)) != hipSuccess) return e;
+    if ((e = launch_dgrad_f32(d1, s)) != hipSuccess) return e;
+    if ((e = launch_wgrad_f32(g1, s)) != hipSuccess) return e;
+  }
+  if ((e = launch_zero_dropped(ly, a.offsets, a.perm, dz_assign, s)) != hipSuccess) return e;
+  return launch_sum_copies(ly, dz_assign, a.dz, s);
+}
+
+// Size limits of the backward on top of check_tokens: 32-bit byte offsets of the bf16 GEMMs
+// (dH is A x 2h), and the fp32 kernels' grid (rows and output rows of a group <= 65535).
+moe_status_t check_backward(const moe_config_t* c, int64_t T) {
+  if (c->expert_precision != MOE_PRECISION_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the experts backward runs in bf16 precision (MXFP8 training is not built)");
+  const int64_t K = c->latent_dim ? c->latent_dim : c->d_model;
+  const int64_t A = T * c->top_k;
+  if (c->dtype == MOE_DTYPE_BF16) {
+    if (A * 2 * c->hidden_size >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "a bf16 backward operand would exceed 4 GiB; split the batch");
+  } else if (A > 65535 || K > 65535 || 2 * c->hidden_size > 65535) {
+    return fail(MOE_ERR_UNSUPPORTED, "the fp32 experts backward serves up to 65535 assignments and widths");
+  }
+  return MOE_OK;
 }
 
 std::mutex g_dev_mu;
@@ -701,6 +887,103 @@ moe_status_t moe_experts_forward(const moe_config_t* c, const moe_weights_t* w, 
   MOE_TRY_HIP(run_experts(ly, z, perm, tiles, small_tiles, w, at<void>(ws, L.act), y_assign, mx_buffers(ws, L), s),
               "experts");
   MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, y_assign, s), "dropped rows");
+  return ok();
+}
+
+moe_status_t moe_experts_forward_train(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* z,
+                                       const int32_t* offsets, const int32_t* perm, void* y_assign, void* h_saved,
+                                       void* act_saved, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = check_backward(c, T)) != MOE_OK) return st;
+  if ((st = check_weights(c, w, false, false, true)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(z, "z")) != MOE_OK) return st;
+  if ((st = need(offsets, "expert_offsets")) != MOE_OK) return st;
+  if ((st = need(perm, "permutation")) != MOE_OK) return st;
+  if ((st = need(y_assign, "y_assign")) != MOE_OK) return st;
+  if ((st = need(h_saved, "h_saved")) != MOE_OK) return st;
+  if ((st = need(act_saved, "act_saved")) != MOE_OK) return st;
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  const WsLayout L = ws_layout(ly);
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const TileList tiles = tiles_of(ws, L);
+  const TileList small_tiles = small_tiles_of(ws, L);
+  MOE_TRY_HIP(launch_build_tiles(ly, offsets, tiles, small_tiles, tile_plan(ly), s), "tile list");
+  MOE_TRY_HIP(run_experts(ly, z, perm, tiles, small_tiles, w, act_saved, y_assign, mx_buffers(ws, L), s, h_saved),
+              "experts");
+  MOE_TRY_HIP(launch_zero_dropped(ly, offsets, perm, y_assign, s), "dropped rows");
+  return ok();
+}
+
+moe_status_t moe_experts_backward_workspace_size(const moe_config_t* c, int64_t T, size_t* bytes) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = check_backward(c, T)) != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_layout(make_layer(c, T)).total;
+  return ok();
+}
+
+moe_status_t moe_experts_backward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* z,
+                                  const int32_t* offsets, const int32_t* perm, const void* h_saved,
+                                  const void* act_saved, const void* dy_assign, void* dz, void* dw1, void* dw2,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if ((st = check_backward(c, T)) != MOE_OK) return st;
+  if ((st = check_weights(c, w, false, false, true)) != MOE_OK) return st;
+  if ((st = need(dw1, "dw1")) != MOE_OK) return st;
+  if ((st = need(dw2, "dw2")) != MOE_OK) return st;
+  if (T > 0) {
+    if ((st = need(offsets, "expert_offsets")) != MOE_OK) return st;
+    if ((st = need(ws, "workspace")) != MOE_OK) return st;
+    if ((st = need(z, "z")) != MOE_OK) return st;
+    if ((st = need(perm, "permutation")) != MOE_OK) return st;
+    if ((st = need(h_saved, "h_saved")) != MOE_OK) return st;
+    if ((st = need(act_saved, "act_saved")) != MOE_OK) return st;
+    if ((st = need(dy_assign, "dy_assign")) != MOE_OK) return st;
+    if ((st = need(dz, "dz")) != MOE_OK) return st;
+  }
+  const Layer ly = make_layer(c, T);
+  const BwdLayout L = bwd_layout(ly);
+  if (T > 0 && ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
+                                                 std::to_string(L.total));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // no rows: the weight gradients are zero
+    MOE_TRY_HIP(launch_fill_zero(dw1, static_cast<size_t>(ly.E) * 2 * ly.h * ly.K * elem_size(ly), s), "dw1");
+    MOE_TRY_HIP(launch_fill_zero(dw2, static_cast<size_t>(ly.E) * ly.K * ly.h * elem_size(ly), s), "dw2");
+    return ok();
+  }
+  const BwdArgs a{z, offsets, perm, h_saved, act_saved, dy_assign, dz, dw1, dw2};
+  MOE_TRY_HIP(run_experts_backward(ly, w, a, ws, L, s), "experts backward");
+  return ok();
+}
+
+moe_status_t moe_combine_backward(const moe_config_t* c, int64_t T, const void* y_assign,
+                                  const float* expert_weights, const void* d_out, void* dy_assign,
+                                  float* d_expert_weights, void* stream) {
+  moe_status_t st = validate_config(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(c, T)) != MOE_OK) return st;
+  if (c->latent_dim && c->up_proj_input_norm)
+    return fail(MOE_ERR_UNSUPPORTED, "the combine backward through the latent RMSNorm is not built");
+  if (T == 0) return ok();
+  if ((st = need(y_assign, "y_assign")) != MOE_OK) return st;
+  if ((st = need(expert_weights, "expert_weights")) != MOE_OK) return st;
+  if ((st = need(d_out, "d_out")) != MOE_OK) return st;
+  if ((st = need(dy_assign, "dy_assign")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  MOE_TRY_HIP(launch_combine_backward(ly, y_assign, expert_weights, d_out, dy_assign, d_expert_weights,
+                                      static_cast<hipStream_t>(stream)),
+              "combine backward");
   return ok();
 }
 

@@ -234,6 +234,25 @@ struct GemmCall {
   // instead of C
   uint8_t* c_codes;
   uint8_t* c_scales;
+  // Training forward: the SwiGLU GEMM also stores its pre-activation H (rows_bound, 2 *
+  // swiglu_h), sorted rows, [up | gate], rounded to bf16 (or NULL).
+  void* h_out;
+  // Backward operand layouts (bf16 MFMA GEMM). trans bit 0: A is stored contraction-major,
+  // A(m, k) at A[k * lda + m]; bit 1: B likewise, B(n, k) at B[k * ldb + n] (per group).
+  int trans;
+  // SwiGLU-backward epilogue (bwd_h > 0): the product is d_act (rows, bwd_h), rounded to bf16;
+  // with the saved H = h_in (rows, 2 * bwd_h) it writes [d_up | d_gate] to C (ldc = 2 * bwd_h).
+  int64_t bwd_h;
+  const void* h_in;
+  // Weight-gradient mode (group_offsets != NULL): for each of `groups` groups g the product
+  // C_g (dense_M, N) = sum over the contraction rows p in [group_offsets[g],
+  // group_offsets[g + 1]) of A(., p) B(., p)^T, A and B both contraction-major (trans = 3);
+  // C_g starts c_group_stride elements after C_{g-1}. Rows past a group's end read zero_row
+  // (at least 512 zero bytes) instead.
+  const int32_t* group_offsets;
+  int32_t groups;
+  int64_t c_group_stride;
+  const void* zero_row;
   // Bounds used to clamp every row index a kernel derives from device data, so that a
   // corrupt index can never address memory outside the operands.
   int64_t a_rows;           // rows of A
@@ -245,6 +264,11 @@ struct GemmCall {
 int gemm_bf16_tile_m(int variant);
 int gemm_bf16_pick_variant(double mean_rows_per_group);
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s);
+// Backward GEMMs (bf16). Input gradients: grouped M-tiles of the given variant's tile height,
+// B contraction-major (trans = 2), epilogue SwiGLU backward (bwd_h > 0), scatter or plain.
+// Weight gradients: trans = 3 with group_offsets (one launch over all groups).
+hipError_t launch_gemm_bf16_dgrad(const GemmCall& c, int variant, hipStream_t s);
+hipError_t launch_gemm_bf16_wgrad(const GemmCall& c, hipStream_t s);
 // Grouped MXFP8 GEMM: A and B are E4M3 codes (1 byte per element, ld in elements = bytes)
 // with E8M0 scales; Kd a multiple of 128; M-tile height gemm_mx_tile_m(). Output and
 // epilogues as launch_gemm_bf16 (SwiGLU + gather, or scatter).
@@ -281,6 +305,22 @@ hipError_t launch_score_bias_update(int E, float gamma, int64_t* acc, float* bia
 // scales (rows, cols / 32); cols a multiple of 32.
 hipError_t launch_mx_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                               hipStream_t s);
+
+// Backward of the routed experts (backward.hip).
+// dst[p] = src[idx[p] / div] for the kept rows p < min(*n_ptr, n_max); rows of row_bytes (a
+// multiple of 16) bytes.
+hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int32_t* idx, int div, const int32_t* n_ptr,
+                              int64_t n_max, int64_t row_bytes, void* dst, hipStream_t s);
+// out (T, K) D = sum over j of in (T*k, K) D rows t*k+j, fp32, j ascending.
+hipError_t launch_sum_copies(const Layer& ly, const void* in, void* out, hipStream_t s);
+// dY (T*k, K) D = w * dO, dw (T, k) f32 = <dO[t], Y[t*k+j]> (dw may be NULL).
+hipError_t launch_combine_backward(const Layer& ly, const void* y_assign, const float* w, const void* d_out,
+                                   void* dy_assign, float* dw, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// fp32 layers: input gradients (group_offsets = expert offsets, groups = E, rows_bound <= 65535)
+// and weight gradients (dense_M <= 65535 output rows per group), see backward.hip.
+hipError_t launch_dgrad_f32(const GemmCall& c, hipStream_t s);
+hipError_t launch_wgrad_f32(const GemmCall& c, hipStream_t s);
 
 // Weighted combine (+ RMSNorm): out (T, K) D.
 hipError_t launch_combine(const Layer& ly, const void* y_assign, const float* w,

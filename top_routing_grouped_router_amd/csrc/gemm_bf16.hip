@@ -162,15 +162,58 @@ __device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, uint32_t s
                                                          static_cast<int>(sb));
 }
 
+// Contraction-major operands (the backward's W^T, dY^T and act^T products): a staged row is one
+// contraction index with the tile's 256 columns (512 bytes, 32 chunks of 16 bytes); chunk c of
+// row r lives in slot c ^ ((r & 3) << 2), so the four rows one transposing read touches per
+// half-wavefront land in four different quarters of the banks.
+constexpr int kTrRowBytes = 512;
+__device__ __forceinline__ int tr_addr(int row, int col) {
+  return row * kTrRowBytes + ((((col >> 3) ^ ((row & 3) << 2))) << 4) + ((col & 7) << 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA fragment (8 consecutive contraction indices of one column) from a contraction-major
+// tile: ds_read_b64_tr_b16 gives lane i of each 16-lane group element (i % 4) of the 8 bytes
+// addressed by lane 4 * j + i / 4 of the group, for j = 0..3. Each lane therefore addresses
+// row (i / 4) and columns 4 * (i % 4) .. +3 of a 4 x 16 block, and receives the four rows of
+// column i: two reads give the 8 contraction indices of the lane's column. Lanes 0-15 / 16-31
+// take columns 0-15 / 16-31 of the 32-column sub-tile at contraction 0-7 of the k16 step, lanes
+// 32-63 the same columns at contraction 8-15 (the MFMA operand layout).
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int col32, int kk, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = col32 + 16 * (g & 1) + 4 * (i & 3);
+  const int row = 16 * kk + 8 * (g >> 1) + (i >> 2);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(row, col)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(row + 4, col)));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int KSTEPS, int KREADS, int KMFMA, int KLOADS>
 __device__ __forceinline__ void sched_stage() {
   __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);  // step-0 reads
   sched_stage_step<0, KSTEPS, KREADS, KMFMA, KLOADS, KLOADS>();
 }
 
-template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false, bool OUT_MX = false>
+// TRANS: bit 0 = the token operand A is contraction-major, bit 1 = the weight operand B is (see
+// GemmCall::trans). WGRAD: weight-gradient mode, the contraction runs over each group's rows
+// (GemmCall::group_offsets). SWIGLU_BWD: the SwiGLU-backward epilogue (GemmCall::bwd_h).
+// H_OUT: the SwiGLU epilogue also stores the pre-activation (GemmCall::h_out).
+template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false, bool OUT_MX = false, int TRANS = 0,
+          bool WGRAD = false, bool SWIGLU_BWD = false, bool H_OUT = false>
 __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
   static_assert(S::NSTAGE == 2, "the persistent loop runs a two-slot ring");
+  constexpr bool TA = (TRANS & 1) != 0, TB = (TRANS & 2) != 0;
+  static_assert(!(TA || TB) || (!S::MX && S::PLANES == 1 && S::BK == 64 && !SWIGLU && !OUT_F32 && !OUT_MX),
+                "contraction-major operands: plain bf16 products");
+  static_assert(!TA || S::BM * 2 == kTrRowBytes, "contraction-major A: 256-column tiles");
+  static_assert(!TB || S::BN * 2 == kTrRowBytes, "contraction-major B: 256-column tiles");
+  static_assert(!WGRAD || (TRANS == 3 && !GATHER && !SCATTER && !SWIGLU_BWD), "weight gradients: both operands contraction-major");
+  static_assert(!SWIGLU_BWD || (!SWIGLU && !SCATTER && !OUT_F32 && !OUT_MX), "SwiGLU backward epilogue");
+  static_assert(!H_OUT || (SWIGLU && !S::MX), "the pre-activation is stored by the bf16 SwiGLU GEMM");
   static_assert(!SWIGLU || S::TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
   static_assert(!SWIGLU || S::PLANES == 1, "planes are for plain products");
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
@@ -182,15 +225,21 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 
   const int64_t cols_per_tile = SWIGLU ? S::BN / 2 : S::BN;
   const int64_t ntn = (c.N + cols_per_tile - 1) / cols_per_tile;
-  const int64_t total_m = c.dense_M > 0 ? (c.dense_M + S::BM - 1) / S::BM
-                                        : min(static_cast<int64_t>(*c.tiles.count),
-                                              static_cast<int64_t>(c.tiles.cap));
+  // weight-gradient mode: every group has the same M-tiles (output rows of one group)
+  const int64_t wg_mtiles = WGRAD ? (c.dense_M + S::BM - 1) / S::BM : 1;
+  const int64_t total_m = WGRAD ? wg_mtiles * c.groups
+                          : c.dense_M > 0 ? (c.dense_M + S::BM - 1) / S::BM
+                                          : min(static_cast<int64_t>(*c.tiles.count),
+                                                static_cast<int64_t>(c.tiles.cap));
   const int64_t total = total_m * ntn;
   const int xcd = blockIdx.x % kXcds;
   const int per_xcd = gridDim.x / kXcds;
   const int64_t chunk = (total + kXcds - 1) / kXcds;
-  const int nk = static_cast<int>(c.Kd / S::BK);
   const unsigned char* Ab = static_cast<const unsigned char*>(c.A);
+  // bytes from one k-stage to the next: along the row, or 64 rows down for a contraction-major
+  // operand
+  const uint32_t a_step = TA ? static_cast<uint32_t>(S::BK * c.lda * 2) : static_cast<uint32_t>(S::ROWB);
+  const uint32_t b_step = TB ? static_cast<uint32_t>(S::BK * c.ldb * 2) : static_cast<uint32_t>(S::ROWB);
   OutT* Cbase = static_cast<OutT*>(c.C);
 
   // this lane's row inside a DMA load
@@ -201,6 +250,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   struct TileState {
     int64_t row0, nt;
     int rows;
+    int nk;                    // k-stages of this tile
+    int kcnt;                  // weight-gradient mode: contraction rows of the tile's group
+    int64_t cofs;              // weight-gradient mode: output offset of the group (elements)
+    const unsigned char* Abase;
     const unsigned char* Bexp;
     uint32_t src_off[S::NQ];  // byte offset of the source 16-byte chunk of load q (k-stage 0)
     const unsigned char* sc_base;  // MXFP8: scale array of this wavefront's 64 staged rows
@@ -219,7 +272,22 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int64_t mt = first_m + local % gm;
     t.nt = local / gm;
     int64_t grp;
-    if (c.dense_M > 0) {
+    t.nk = static_cast<int>(c.Kd / S::BK);
+    t.kcnt = 0;
+    t.cofs = 0;
+    t.Abase = Ab;
+    if (WGRAD) {
+      grp = mt / wg_mtiles;
+      t.row0 = (mt - grp * wg_mtiles) * S::BM;
+      t.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - t.row0));
+      const int64_t kb = min(max(static_cast<int64_t>(c.group_offsets[grp]), int64_t(0)), c.rows_bound);
+      const int64_t ke = min(max(static_cast<int64_t>(c.group_offsets[grp + 1]), kb), c.rows_bound);
+      t.kcnt = static_cast<int>(ke - kb);
+      t.nk = (t.kcnt + S::BK - 1) / S::BK;
+      t.cofs = grp * c.c_group_stride;
+      t.Abase = Ab + kb * c.lda * 2;
+      t.Bexp = static_cast<const unsigned char*>(c.B) + kb * c.ldb * 2;
+    } else if (c.dense_M > 0) {
       t.row0 = mt * S::BM;
       t.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - t.row0));
       grp = 0;
@@ -228,11 +296,23 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       t.rows = c.tiles.rows[mt];
       grp = c.tiles.expert[mt];
     }
-    t.Bexp = static_cast<const unsigned char*>(c.B) + grp * c.b_group_stride * S::EB;
+    if (!WGRAD) t.Bexp = static_cast<const unsigned char*>(c.B) + grp * c.b_group_stride * S::EB;
 #pragma unroll
     for (int q = 0; q < S::NQ; ++q) {
       const int i = wave + S::NW * q;
       const bool is_a = load_is_a(q);
+      if ((is_a && TA) || (!is_a && TB)) {
+        // contraction-major: this lane fetches 16 bytes of staged row tr (contraction index),
+        // logical chunk tc, into the linear DMA slot
+        const int il = is_a ? i : i - S::BM / S::kRowsPerDma;
+        const int tr = 2 * il + (lane >> 5);
+        const int tc = (lane & 31) ^ ((tr & 3) << 2);
+        const int64_t width = is_a ? c.dense_M : c.N;    // columns of the operand
+        const int64_t col0 = is_a ? t.row0 : t.nt * S::BN;
+        const int64_t col = min(col0 + 8 * tc, width - 8);
+        t.src_off[q] = static_cast<uint32_t>((tr * (is_a ? c.lda : c.ldb) + col) * 2);
+        continue;
+      }
       const int r = (is_a ? i : i - S::BM / S::kRowsPerDma) * S::kRowsPerDma + dma_row;
       // the logical chunk this lane fetches, so that the linear LDS write lands swizzled
       const int chunk_l = (lane % S::CHUNKS) ^ ((r / S::ROWS_PER_BANKLINE) & (S::CHUNKS - 1));
@@ -297,8 +377,15 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int q = 0; q < S::NQ; ++q) {
       const int i = wave + S::NW * q;
       if (S::NI % S::NW != 0 && i >= S::NI) continue;
-      const unsigned char* g =
-          (load_is_a(q) ? Ab : t.Bexp) + (t.src_off[q] + static_cast<uint32_t>(kt) * S::ROWB);
+      const bool is_a = load_is_a(q);
+      const unsigned char* g = (is_a ? (WGRAD ? t.Abase : Ab) : t.Bexp) +
+                               (t.src_off[q] + static_cast<uint32_t>(kt) * (is_a ? a_step : b_step));
+      if (WGRAD) {
+        // contraction rows past the group's end read zeros
+        const int il = is_a ? i : i - S::BM / S::kRowsPerDma;
+        if (kt * S::BK + 2 * il + (lane >> 5) >= t.kcnt)
+          g = static_cast<const unsigned char*>(c.zero_row) + (lane & 31) * 16;
+      }
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
     }
     if constexpr (S::MX) {
@@ -349,12 +436,20 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int pl = 0; pl < S::PLANES; ++pl)
 #pragma unroll
-      for (int j = 0; j < S::TN; ++j)
-        fw[fs][pl][j] = *reinterpret_cast<const bf16x8*>(
-            lb + swz<S>(pl * S::BN + wn * S::TN * 32 + j * 32 + (lane & 31), ch));
+      for (int j = 0; j < S::TN; ++j) {
+        if constexpr (TB)
+          fw[fs][pl][j] = tr_frag(lb, wn * S::TN * 32 + j * 32, kk, lane);
+        else
+          fw[fs][pl][j] = *reinterpret_cast<const bf16x8*>(
+              lb + swz<S>(pl * S::BN + wn * S::TN * 32 + j * 32 + (lane & 31), ch));
+      }
 #pragma unroll
-    for (int i = 0; i < S::TM; ++i)
-      ft[fs][i] = *reinterpret_cast<const bf16x8*>(la + swz<S>(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
+    for (int i = 0; i < S::TM; ++i) {
+      if constexpr (TA)
+        ft[fs][i] = tr_frag(la, wm * S::TM * 32 + i * 32, kk, lane);
+      else
+        ft[fs][i] = *reinterpret_cast<const bf16x8*>(la + swz<S>(wm * S::TM * 32 + i * 32 + (lane & 31), ch));
+    }
   };
 
   // Epilogue, staged through LDS slot 1 (slot 0 is receiving the next tile's first stage).
@@ -429,6 +524,25 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
                 o[r] = f32_to_bf16_bits(up * gate * __builtin_amdgcn_rcpf(1.f + e));
               }
               const int ct = wn * (S::TN * 16) + j * 32 + 8 * g + quad;
+              if constexpr (H_OUT) {
+                // training forward: the pre-activation H (bf16, [up | gate]) of this lane's
+                // 4 columns, stored straight from the registers
+                const int m = wm * S::TM * 32 + i * 32 + (lane & 31);
+                const int64_t hc = col0 + ct;
+                if (m < t.rows && hc < c.N) {
+                  uint16_t* hr = static_cast<uint16_t*>(c.h_out) + min(t.row0 + m, c.rows_bound - 1) * 2 * c.swiglu_h;
+                  uint32_t u[2], gv[2];
+#pragma unroll
+                  for (int r = 0; r < 2; ++r) {
+                    u[r] = f32_to_bf16_bits(acc[i][j][4 * g + 2 * r]) |
+                           (static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * g + 2 * r + 1])) << 16);
+                    gv[r] = f32_to_bf16_bits(acc[i][j + S::TN / 2][4 * g + 2 * r]) |
+                            (static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j + S::TN / 2][4 * g + 2 * r + 1])) << 16);
+                  }
+                  *reinterpret_cast<uint2*>(hr + hc) = make_uint2(u[0], u[1]);
+                  *reinterpret_cast<uint2*>(hr + c.swiglu_h + hc) = make_uint2(gv[0], gv[1]);
+                }
+              }
               *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
                   make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
                              o[2] | (static_cast<uint32_t>(o[3]) << 16));
@@ -466,14 +580,44 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       for (int k = 0; k < KI; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg_addr(k * RPI + tid / CPR, cc * 16));
       if (rho == NR - 1 && more) {
         setup(it_next, nx);
-        issue(nx, 0, 0);
+        if (!WGRAD || nx.nk > 0) issue(nx, 0, 0);
       }
 #pragma unroll
       for (int k = 0; k < KI; ++k) {
         const int lr = k * RPI + tid / CPR;
         const int m = tile_row(rho, lr);
         const int64_t orow = SCATTER ? static_cast<int64_t>(sidx[SCATTER ? k : 0]) : t.row0 + m;
-        if constexpr (OUT_MX) {
+        if constexpr (SWIGLU_BWD) {
+          // v holds 8 columns of d_act (bf16) of sorted row orow; with the saved up / gate of
+          // those columns: d_up = d_act * silu(gate), d_gate = d_act * up * silu'(gate),
+          // silu' = sigmoid * (1 + gate * (1 - sigmoid)), in fp32, stored as bf16.
+          if (m < t.rows && col < c.N) {
+            const int64_t p = min(max(orow, int64_t(0)), c.rows_bound - 1);
+            const uint16_t* hr = static_cast<const uint16_t*>(c.h_in) + p * 2 * c.bwd_h;
+            const u32x4_t hu = *reinterpret_cast<const u32x4_t*>(hr + col);
+            const u32x4_t hg = *reinterpret_cast<const u32x4_t*>(hr + c.bwd_h + col);
+            u32x4_t du, dg;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              uint32_t ou[2], og[2];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const float d = __uint_as_float(hh ? (v[k][w] & 0xFFFF0000u) : (v[k][w] << 16));
+                const float up = __uint_as_float(hh ? (hu[w] & 0xFFFF0000u) : (hu[w] << 16));
+                const float gate = __uint_as_float(hh ? (hg[w] & 0xFFFF0000u) : (hg[w] << 16));
+                const float e = __builtin_amdgcn_exp2f(-gate * 1.44269504088896340736f);
+                const float sig = __builtin_amdgcn_rcpf(1.f + e);
+                ou[hh] = f32_to_bf16_bits(d * (gate * sig));
+                og[hh] = f32_to_bf16_bits(d * up * (sig * (1.f + gate * (1.f - sig))));
+              }
+              du[w] = ou[0] | (ou[1] << 16);
+              dg[w] = og[0] | (og[1] << 16);
+            }
+            uint16_t* dr = reinterpret_cast<uint16_t*>(Cbase) + p * c.ldc;
+            *reinterpret_cast<u32x4_t*>(dr + col) = du;
+            *reinterpret_cast<u32x4_t*>(dr + c.bwd_h + col) = dg;
+          }
+        } else if constexpr (OUT_MX) {
           // MXFP8 output (the bf16 values staged above, quantised as the standalone quantiser
           // does): a 32-column block is the 16-byte chunks of 4 adjacent lanes of one row;
           // its amax comes from two lane exchanges inside the group, executed by every lane.
@@ -498,7 +642,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           }
         } else {
           if (m < t.rows && col < c.N)
-            *reinterpret_cast<u32x4_t*>(Cbase + min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col) = v[k];
+            *reinterpret_cast<u32x4_t*>(Cbase + (WGRAD ? t.cofs : 0) + min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col) = v[k];
         }
       }
     }
@@ -511,7 +655,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   if (it >= chunk || xcd * chunk + it >= total) return;
   TileState cur;
   setup(it, cur);
-  issue(cur, 0, 0);
+  if (!WGRAD || cur.nk > 0) issue(cur, 0, 0);
   for (;;) {
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
@@ -520,6 +664,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    const int nk = WGRAD ? cur.nk : static_cast<int>(c.Kd / S::BK);
     for (int kt = 0; kt < nk; ++kt) {
       // This wavefront's loads of stage kt have landed; after the barrier so have every
       // wavefront's, and every wavefront is done reading stage kt-1, whose slot is refilled.
@@ -546,7 +691,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         }
       } else {
         constexpr int kSteps = S::BK / 16;
-        constexpr int kReads = S::TM + S::PLANES * S::TN;  // LDS fragment reads per k16 step
+        // LDS fragment reads per k16 step (a contraction-major fragment takes two)
+        constexpr int kReads = (TA ? 2 : 1) * S::TM + (TB ? 2 : 1) * S::PLANES * S::TN;
         constexpr int kMfma = S::TM * S::TN * S::PLANES;   // MFMAs per k16 step
         lds_frags(0, la, lb, 0);
 #pragma unroll
@@ -602,7 +748,11 @@ hipError_t launch_shape(const GemmCall& c, hipStream_t s, int wg_per_cu) {
   grid = ((grid + kXcds - 1) / kXcds) * kXcds;  // whole XCD rounds
   const dim3 g(static_cast<unsigned>(grid)), b(S::NT);
   const bool sw = c.swiglu_h > 0, ga = c.gather != nullptr, sc = c.scatter != nullptr;
-  if (sw && ga && !sc) hipLaunchKernelGGL((gemm_bf16_kernel<S, true, true, false>), g, b, 0, s, c);
+  if (c.h_out && !(sw && ga && !sc && !S::MX)) return hipErrorInvalidValue;
+  if (sw && ga && !sc && c.h_out) {
+    if constexpr (!S::MX)
+      hipLaunchKernelGGL((gemm_bf16_kernel<S, true, true, false, false, false, 0, false, false, true>), g, b, 0, s, c);
+  } else if (sw && ga && !sc) hipLaunchKernelGGL((gemm_bf16_kernel<S, true, true, false>), g, b, 0, s, c);
   else if (!sw && !ga && sc) hipLaunchKernelGGL((gemm_bf16_kernel<S, false, false, true>), g, b, 0, s, c);
   else if (!sw && !ga && !sc) hipLaunchKernelGGL((gemm_bf16_kernel<S, false, false, false>), g, b, 0, s, c);
   else return hipErrorInvalidValue;
@@ -650,6 +800,52 @@ hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s) {
   if (variant == 0) return launch_shape<ShapeLarge>(c, s, ShapeLarge::WG_PER_CU);
   return launch_shape<ShapeSmall>(c, s, ShapeSmall::WG_PER_CU);
+}
+
+namespace {
+
+// Input gradients: grouped rows like the forward, weights read contraction-major (W[e] as
+// stored is (contraction, N)). Epilogue: SwiGLU backward, scatter, or plain rows.
+template <class S>
+hipError_t launch_dgrad_shape(const GemmCall& c, hipStream_t s) {
+  const int64_t ntn = (c.N + S::BN - 1) / S::BN;
+  const int64_t upper = static_cast<int64_t>(c.tiles.cap) * ntn;
+  if (upper <= 0 || c.rows_bound <= 0) return hipSuccess;
+  int64_t grid = std::min<int64_t>(upper, static_cast<int64_t>(device_cu_count()) * S::WG_PER_CU);
+  grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+  const dim3 g(static_cast<unsigned>(grid)), b(S::NT);
+  if (c.bwd_h > 0) {
+    if (c.scatter || !c.h_in) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_kernel<S, false, false, false, false, false, 2, false, true>), g, b, 0, s, c);
+  } else if (c.scatter) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<S, false, false, true, false, false, 2>), g, b, 0, s, c);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_kernel<S, false, false, false, false, false, 2>), g, b, 0, s, c);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_dgrad(const GemmCall& c, int variant, hipStream_t s) {
+  if (c.trans != 2 || c.gather || c.swiglu_h > 0 || c.group_offsets || c.dense_M > 0 || c.N % 8 != 0)
+    return hipErrorInvalidValue;
+  if (variant == 0) return launch_dgrad_shape<ShapeLarge>(c, s);
+  return launch_dgrad_shape<ShapeSmall>(c, s);
+}
+
+hipError_t launch_gemm_bf16_wgrad(const GemmCall& c, hipStream_t s) {
+  using S = ShapeLarge;
+  if (c.trans != 3 || !c.group_offsets || !c.zero_row || c.gather || c.scatter || c.bwd_h > 0 || c.swiglu_h > 0 ||
+      c.dense_M <= 0 || c.groups <= 0 || c.N <= 0 || c.N % 8 != 0 || c.dense_M % 8 != 0)
+    return hipErrorInvalidValue;
+  const int64_t ntn = (c.N + S::BN - 1) / S::BN;
+  const int64_t upper = static_cast<int64_t>(c.groups) * ((c.dense_M + S::BM - 1) / S::BM) * ntn;
+  int64_t grid = std::min<int64_t>(upper, static_cast<int64_t>(device_cu_count()) * S::WG_PER_CU);
+  grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+  hipLaunchKernelGGL((gemm_bf16_kernel<S, false, false, false, false, false, 3, true>), dim3(static_cast<unsigned>(grid)),
+                     dim3(S::NT), 0, s, c);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -111,6 +111,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmCall c, const float* 
           if (col >= c.N) continue;
           const float up = acc[i][j], gate = acc[i][j + 2];
           C[orow * c.ldc + col] = up * (gate / (1.f + expf(-gate)));
+          if (c.h_out) {  // training forward: the pre-activation [up | gate] of sorted row pr
+            float* hr = static_cast<float*>(c.h_out) + pr * 2 * c.swiglu_h;
+            hr[col] = up;
+            hr[c.swiglu_h + col] = gate;
+          }
         }
       } else {
 #pragma unroll
