@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the extra measurement of the same layer with MXFP8 expert matmuls")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the extra measurement of the routed experts' backward")
     ap.add_argument("--stages", action="store_true", help="also time each stage call alone")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference the HBM "
@@ -115,8 +117,13 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
     def gemm_kind(name):
         if "gemm_bf16_kernel" not in name:
             return None
+        # template arguments after the tile shape: SWIGLU, GATHER, SCATTER, then the output,
+        # operand-layout and epilogue options, all off for the two forward GEMMs
         tail = name.split(">", 1)[1] if ">" in name else name
-        flags = [t.strip() for t in tail.split(",")][1:4]
+        flags = [t.strip() for t in tail.split(">")[0].split(",")][1:]
+        rest = flags[3:]
+        if any(f not in ("false", "0") for f in rest):
+            return None
         if flags[:3] == ["true", "true", "false"]:
             return "gemm1"
         if flags[:3] == ["false", "false", "true"]:
@@ -290,6 +297,34 @@ def main():
                                 "stage_ms": round(g8, 4), "achieved_tflops": round(a8, 1),
                                 "peak_tflops": PEAK_FP8_TFLOPS, "frac": round(a8 / PEAK_FP8_TFLOPS, 4)}
         del layer8, w8
+    if args.precision == "bf16" and not args.no_backward:
+        # The routed experts' backward on the same routing (an extra record): input gradient of
+        # the activation with the SwiGLU backward fused, w2's weight gradient, the input
+        # gradient of z (scattered per copy, then summed per token) and w1's weight gradient.
+        # Saved tensors from the training forward; output and workspace allocated outside the
+        # timed region.
+        fw = moe.experts_forward_train(cfg, w, z, offs, perm)
+        dy = torch.randn(fw["y_assign"].shape, device="cuda").mul_(0.5).to(x.dtype)
+        bws = torch.empty(moe.experts_backward_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+        grads = {"dz": torch.empty_like(z), "dw1": torch.empty_like(w["w1"]), "dw2": torch.empty_like(w["w2"])}
+        run_bwd = lambda: moe.experts_backward(cfg, w, z, offs, perm, fw, dy, workspace=bws, out=grads)  # noqa: E731
+        for _ in range(2):
+            run_bwd()
+        bms = event_time_ms(run_bwd, max(args.steps, 5), torch)
+        ftms = event_time_ms(lambda: moe.experts_forward_train(cfg, w, z, offs, perm), max(args.steps, 5), torch)
+        cbms = None
+        if not (L and cfg.get("up_proj_input_norm", True)):  # no backward through the latent norm
+            o_grad = torch.randn((T, K), device="cuda").to(x.dtype)
+            cbms = event_time_ms(lambda: moe.combine_backward(cfg, fw["y_assign"], r["expert_weights"], o_grad), 5,
+                                 torch)
+        bflops = 12.0 * A * K * h
+        ab = bflops / (bms / 1e3) / 1e12
+        out["experts_backward"] = {"value": round(T / (bms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(bms, 4),
+                                   "flops_per_launch": bflops, "achieved_tflops": round(ab, 1),
+                                   "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(ab / PEAK_BF16_TFLOPS, 4),
+                                   "forward_train_ms": round(ftms, 4),
+                                   "combine_backward_ms": None if cbms is None else round(cbms, 4)}
+        del fw, dy, bws, grads
     if args.stages:
         st = {}
         st["router"] = event_time_ms(lambda: moe.router_forward(cfg, w, x, logits=False, scores=False), 5, torch)
