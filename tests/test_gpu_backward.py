@@ -217,59 +217,68 @@ def test_combine_backward(case):
     assert np.all(np.abs(dw - ref["dw"]) <= K * 2.0 ** -24 * M + 1e-30), np.abs(dw - ref["dw"]).max()
 
 
-def test_full_size_backward_sampled():
-    """olmoe at its full size (8192 tokens, 64 experts, top-8, 2048 x 1024) in the launch
-    configuration the bench times: every token's dz against properties, sampled tokens' dz
-    and two experts' weight gradients against the oracle, which recomputes everything for those
-    rows from the inputs (the GPU's saved tensors come from the GPU's training forward)."""
-    banner("full-size backward olmoe")
-    cfg, w, x = workloads.make_workload("olmoe", device="cuda")
+@pytest.mark.parametrize("name,skew", [("olmoe", 0.0), ("latent896", 0.0), ("skewed", 1.0)])
+def test_full_size_backward_sampled(name, skew):
+    """The experts stage at a workload's full size (tokens, experts, top-k, expert width K and
+    hidden width), in the launch configuration the bench times: z, the routing and dY drawn by
+    seeded generators (skewed: indices tilted towards low experts), the GPU's training forward
+    and backward; every gradient finite, 48 sampled tokens' dz and two experts' whole dW1, dW2
+    against the oracle, which recomputes everything for those rows from the inputs."""
+    banner(f"full-size backward {name}")
+    cfg = workloads.layer_config(name)
     cfgO = O.MoEConfig.from_dict(cfg)
-    T, k, E, K, h = x.shape[0], cfg["top_k"], cfg["num_experts"], cfg["d_model"], cfg["hidden_size"]
-    idx = workloads.random_distinct_indices(T, E, k, seed=9).numpy()
+    T, k, E, h = workloads.tokens_of(name), cfg["top_k"], cfg["num_experts"], cfg["hidden_size"]
+    K = cfgO.expert_dim
+    _, w, _ = workloads.make_workload(name, tokens=1, device="cuda")  # weights only
+    D = workloads.storage_dtype(cfg)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    z = torch.randn((T, K), generator=g, device="cuda").to(D)
+    dY = torch.randn((T * k, K), generator=g, device="cuda").mul_(0.5).to(D)
+    idx = workloads.random_distinct_indices(T, E, k, seed=9, skew=skew).numpy()
     counts = O.expert_counts(idx, E)
     offs = O.expert_offsets(counts)
     perm, inv, _ = O.capacity_permutation(idx, E, None)
-    D = workloads.storage_dtype(cfg)
-    g = torch.Generator(device="cuda").manual_seed(21)
-    dY = torch.randn((T * k, K), generator=g, device="cuda").mul_(0.5).to(D)
     wd = to_device_weights(w)
-    fw = moe.experts_forward_train(cfg, wd, x, _idx(offs), _idx(perm))
-    got = moe.experts_backward(cfg, wd, x, _idx(offs), _idx(perm), fw, dY)
+    fw = moe.experts_forward_train(cfg, wd, z, _idx(offs), _idx(perm))
+    got = moe.experts_backward(cfg, wd, z, _idx(offs), _idx(perm), fw, dY)
     torch.cuda.synchronize()
     for key in ("dz", "dw1", "dw2"):
         assert torch.isfinite(got[key].float()).all(), key
-    xs = np32(x)
-    dYn = np32(dY)
-    # sampled tokens: the oracle's own forward and backward on those tokens' assignments
-    sample = np.random.default_rng(4).choice(T, 48, replace=False)
+    print(f"  T={T} E={E} K={K} h={h} rows per expert min {counts.min()} max {counts.max()}", flush=True)
+    rng = np.random.default_rng(4)
+    sample = rng.choice(T, 48, replace=False)
+    zs = np32(z[torch.from_numpy(sample).cuda()]).astype(np.float64)
     used = np.unique(idx[sample])
-    w1 = {int(e): np32(w["w1"][int(e)]) for e in used}
-    w2 = {int(e): np32(w["w2"][int(e)]) for e in used}
+    w1 = {int(e): np32(w["w1"][int(e)]).astype(np.float64) for e in used}
+    w2 = {int(e): np32(w["w2"][int(e)]).astype(np.float64) for e in used}
+    dY_s = np32(dY[torch.from_numpy((sample[:, None] * k + np.arange(k)).ravel()).cuda()]).astype(np.float64)
     dz_ref, Mdz = [], []
-    for t in sample:
+    for i, t in enumerate(sample):
         acc, m = np.zeros(K), np.zeros(K)
         for j in range(k):
             e = int(idx[t, j])
-            r = O.expert_mlp_train(cfgO, xs[t:t + 1], w1[e], w2[e])
-            d_act = O.round_to(dYn[t * k + j:t * k + j + 1].astype(np.float64) @ w2[e].astype(np.float64), "bf16")
+            r = O.expert_mlp_train(cfgO, zs[i:i + 1], w1[e], w2[e])
+            d_act = O.round_to(dY_s[i * k + j:i * k + j + 1] @ w2[e], "bf16")
             dH = O.swiglu_backward(cfgO, r["H"], d_act)
-            acc += O.round_to(dH @ w1[e].astype(np.float64), "bf16")[0]
-            m += (np.abs(dH) @ np.abs(w1[e].astype(np.float64)))[0]
+            acc += O.round_to(dH @ w1[e], "bf16")[0]
+            m += (np.abs(dH) @ np.abs(w1[e]))[0]
         dz_ref.append(O.round_to(acc, "bf16"))
         Mdz.append(m)
-    assert_grad_close(np32(got["dz"])[sample], np.array(dz_ref), np.array(Mdz), "bf16", "dz (sampled tokens)")
-    # two experts' weight gradients: the smallest and one other, from all their rows
-    for e in (int(np.argmin(counts)), int(np.argsort(counts)[E // 2])):
+    assert_grad_close(np32(got["dz"][torch.from_numpy(sample).cuda()]), np.array(dz_ref), np.array(Mdz), "bf16",
+                      "dz (sampled tokens)")
+    # two experts' weight gradients from all their rows: the smallest non-empty expert and a
+    # median one
+    nonempty = np.nonzero(counts)[0]
+    order = nonempty[np.argsort(counts[nonempty], kind="stable")]
+    for e in (int(order[0]), int(order[len(order) // 2])):
         R = perm[offs[e]:offs[e + 1]]
-        toks = R // k
+        Rt = torch.from_numpy(R.astype(np.int64)).cuda()
+        ze = np32(z[Rt // k]).astype(np.float64)
+        dYe = np32(dY[Rt]).astype(np.float64)
         w1e, w2e = np32(w["w1"][e]).astype(np.float64), np32(w["w2"][e]).astype(np.float64)
-        r = O.expert_mlp_train(cfgO, xs[toks], w1e, w2e)
-        dYe = dYn[R].astype(np.float64)
-        d_act = O.round_to(dYe @ w2e, "bf16")
-        dH = O.swiglu_backward(cfgO, r["H"], d_act)
-        dw2 = O.round_to(dYe.T @ r["act"], "bf16")
-        dw1 = O.round_to(dH.T @ xs[toks].astype(np.float64), "bf16")
-        assert_grad_close(np32(got["dw2"][e]), dw2, np.abs(dYe).T @ np.abs(r["act"]), "bf16", f"dw2[{e}]")
-        assert_grad_close(np32(got["dw1"][e]), dw1, np.abs(dH).T @ np.abs(xs[toks].astype(np.float64)), "bf16",
-                          f"dw1[{e}]")
+        r = O.expert_mlp_train(cfgO, ze, w1e, w2e)
+        dH = O.swiglu_backward(cfgO, r["H"], O.round_to(dYe @ w2e, "bf16"))
+        assert_grad_close(np32(got["dw2"][e]), O.round_to(dYe.T @ r["act"], "bf16"), np.abs(dYe).T @ np.abs(r["act"]),
+                          "bf16", f"dw2[{e}] ({R.size} rows)")
+        assert_grad_close(np32(got["dw1"][e]), O.round_to(dH.T @ ze, "bf16"), np.abs(dH).T @ np.abs(ze), "bf16",
+                          f"dw1[{e}] ({R.size} rows)")
