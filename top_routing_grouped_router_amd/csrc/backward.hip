@@ -136,6 +136,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* __restrict__ p, i
     p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// Experts by decreasing row count (ties by index): the rank of expert e is the number of
+// experts with more rows, plus those with as many rows and a lower index. One workgroup,
+// E <= 1024.
+__global__ __launch_bounds__(1024) void expert_order_kernel(const int32_t* __restrict__ offsets, int E,
+                                                            int32_t* __restrict__ order) {
+  __shared__ int32_t cnt[1024];
+  const int e = threadIdx.x;
+  if (e < E) cnt[e] = offsets[e + 1] - offsets[e];
+  __syncthreads();
+  if (e >= E) return;
+  const int32_t c = cnt[e];
+  int rank = 0;
+  for (int f = 0; f < E; ++f) rank += (cnt[f] > c) || (cnt[f] == c && f < e);
+  order[rank] = e;
+}
+
 // expert of sorted row p: the last e with offsets[e] <= p (offsets non-decreasing)
 __device__ int expert_of_row(const int32_t* offsets, int E, int64_t p) {
   int lo = 0, hi = E - 1;
@@ -236,6 +252,12 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (bytes % 16 != 0) return hipErrorInvalidValue;
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_of(n16, 256)), dim3(256), 0, s, static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order, hipStream_t s) {
+  if (E <= 0 || E > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(1024), 0, s, offsets, E, order);
   return hipGetLastError();
 }
 

@@ -253,6 +253,10 @@ struct GemmCall {
   int32_t groups;
   int64_t c_group_stride;
   const void* zero_row;
+  // ... whose tiles are handed out in the order of group_order (groups by decreasing row count;
+  // NULL = 0..groups-1) through tile_counter, one int32 that must be 0 at launch.
+  const int32_t* group_order;
+  int32_t* tile_counter;
   // Bounds used to clamp every row index a kernel derives from device data, so that a
   // corrupt index can never address memory outside the operands.
   int64_t a_rows;           // rows of A
@@ -317,6 +321,9 @@ hipError_t launch_sum_copies(const Layer& ly, const void* in, void* out, hipStre
 hipError_t launch_combine_backward(const Layer& ly, const void* y_assign, const float* w, const void* d_out,
                                    void* dy_assign, float* dw, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// order (E): the experts by decreasing row count offsets[e+1] - offsets[e], ties by index
+// (E <= 1024).
+hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order, hipStream_t s);
 // fp32 layers: input gradients (group_offsets = expert offsets, groups = E, rows_bound <= 65535)
 // and weight gradients (dense_M <= 65535 output rows per group), see backward.hip.
 hipError_t launch_dgrad_f32(const GemmCall& c, hipStream_t s);

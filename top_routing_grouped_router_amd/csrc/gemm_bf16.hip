@@ -262,15 +262,29 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // The load index inside a stage is uniform per wavefront, so is the operand it reads.
   auto load_is_a = [&](int q) { return wave + S::NW * q < S::BM / S::kRowsPerDma; };
 
+  // it: the tile's slot in this XCD's chunk, or (weight-gradient mode) its index in the
+  // heavy-first sequence handed out by the tile counter
   auto setup = [&](int64_t it, TileState& t) {
-    const int64_t lin = xcd * chunk + it;
-    // tiles go in groups of kGroupM M-tiles x all N-tiles
-    const int64_t gsz = kGroupM * ntn;
-    const int64_t grp_i = lin / gsz, first_m = grp_i * kGroupM;
-    const int64_t gm = min(static_cast<int64_t>(kGroupM), total_m - first_m);
-    const int64_t local = lin - grp_i * gsz;
-    const int64_t mt = first_m + local % gm;
-    t.nt = local / gm;
+    int64_t mt;
+    if (WGRAD) {
+      // groups in the given order (most rows first), each group's M-tiles x N-tiles in turn
+      const int64_t per_group = wg_mtiles * ntn;
+      const int64_t r = it / per_group, local = it - r * per_group;
+      const int64_t g = c.group_order ? min(max(static_cast<int64_t>(c.group_order[r]), int64_t(0)),
+                                            static_cast<int64_t>(c.groups) - 1)
+                                      : r;
+      mt = g * wg_mtiles + local / ntn;
+      t.nt = local % ntn;
+    } else {
+      const int64_t lin = xcd * chunk + it;
+      // tiles go in groups of kGroupM M-tiles x all N-tiles
+      const int64_t gsz = kGroupM * ntn;
+      const int64_t grp_i = lin / gsz, first_m = grp_i * kGroupM;
+      const int64_t gm = min(static_cast<int64_t>(kGroupM), total_m - first_m);
+      const int64_t local = lin - grp_i * gsz;
+      mt = first_m + local % gm;
+      t.nt = local / gm;
+    }
     int64_t grp;
     t.nk = static_cast<int>(c.Kd / S::BK);
     t.kcnt = 0;
@@ -651,8 +665,21 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // Persistent loop over this workgroup's tiles: it = slot, slot + per_xcd, ... inside the
   // XCD's chunk. Stage 0 of the next tile is issued before the current tile's epilogue, so its
   // load latency hides under the epilogue's stores.
-  int64_t it = blockIdx.x / kXcds;
-  if (it >= chunk || xcd * chunk + it >= total) return;
+  // Weight-gradient tiles differ in cost (a group's contraction is its row count), so they are
+  // handed out instead: thread 0 takes the next index from the zeroed tile counter when a tile
+  // starts and passes it through LDS (two slots, alternating: a slot is rewritten two tiles
+  // later, after barriers every wavefront has passed); the sequence puts the largest groups
+  // first. Every workgroup leaves once the counter passes the last tile.
+  int32_t* sched = nullptr;
+  if constexpr (WGRAD) {
+    __shared__ int32_t s_sched[2];
+    sched = s_sched;
+    if (tid == 0) s_sched[0] = atomicAdd(c.tile_counter, 1);
+    __syncthreads();
+  }
+  int64_t it = WGRAD ? static_cast<int64_t>(sched[0]) : blockIdx.x / kXcds;
+  if (WGRAD ? it >= total : (it >= chunk || xcd * chunk + it >= total)) return;
+  int parity = 1;
   TileState cur;
   setup(it, cur);
   if (!WGRAD || cur.nk > 0) issue(cur, 0, 0);
@@ -664,6 +691,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    if (WGRAD && tid == 0) sched[parity] = atomicAdd(c.tile_counter, 1);
     const int nk = WGRAD ? cur.nk : static_cast<int>(c.Kd / S::BK);
     for (int kt = 0; kt < nk; ++kt) {
       // This wavefront's loads of stage kt have landed; after the barrier so have every
@@ -710,11 +738,25 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       }
     }
     // Every wavefront done reading this tile's last stages: slot 0 is free for the next tile.
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
+    // (Weight-gradient mode: a full workgroup barrier with fences, which also publishes the
+    // next tile index thread 0 wrote to LDS; no vector-memory load is in flight here.)
+    if constexpr (WGRAD) {
+      __syncthreads();
+    } else {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+    }
 
-    const int64_t it_next = it + per_xcd;
-    const bool more = it_next < chunk && xcd * chunk + it_next < total;
+    int64_t it_next;
+    bool more;
+    if constexpr (WGRAD) {
+      it_next = sched[parity];  // written at this tile's start, before the barrier above
+      more = it_next < total;
+      parity ^= 1;
+    } else {
+      it_next = it + per_xcd;
+      more = it_next < chunk && xcd * chunk + it_next < total;
+    }
     TileState nxt;
     epilogue(cur, more, it_next, nxt);
     if (!more) break;
@@ -836,7 +878,8 @@ hipError_t launch_gemm_bf16_dgrad(const GemmCall& c, int variant, hipStream_t s)
 
 hipError_t launch_gemm_bf16_wgrad(const GemmCall& c, hipStream_t s) {
   using S = ShapeLarge;
-  if (c.trans != 3 || !c.group_offsets || !c.zero_row || c.gather || c.scatter || c.bwd_h > 0 || c.swiglu_h > 0 ||
+  if (c.trans != 3 || !c.group_offsets || !c.zero_row || !c.tile_counter || c.gather || c.scatter || c.bwd_h > 0 ||
+      c.swiglu_h > 0 ||
       c.dense_M <= 0 || c.groups <= 0 || c.N <= 0 || c.N % 8 != 0 || c.dense_M % 8 != 0)
     return hipErrorInvalidValue;
   const int64_t ntn = (c.N + S::BN - 1) / S::BN;
