@@ -655,8 +655,12 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             if ((cc & 3) == 0) c.c_scales[r * (c.N / 32) + col / 32] = static_cast<uint8_t>(sc);
           }
         } else {
+          // Non-temporal: every CU writes its tile in the same burst at the end of a round of
+          // tiles; streaming the rows past the caches keeps the operand lines the next tiles read.
           if (m < t.rows && col < c.N)
-            *reinterpret_cast<u32x4_t*>(Cbase + (WGRAD ? t.cofs : 0) + min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col) = v[k];
+            __builtin_nontemporal_store(
+                v[k], reinterpret_cast<u32x4_t*>(Cbase + (WGRAD ? t.cofs : 0) +
+                                                 min(max(orow, int64_t(0)), c.c_rows - 1) * c.ldc + col));
         }
       }
     }
