@@ -9,8 +9,7 @@
 //   * section "Латентная проекция экспертов": with a latent projection, the up-projection
 //     input is normalised (bias-free RMSNorm by default: n = o / sqrt(mean(o^2) + eps) * g)
 //     and cast to the up-projection weight's dtype.
-// One block per token, 16-byte loads and stores, fp32 math. HBM-bound: it reads k*K and
-// writes K elements per token.
+// 16-byte loads and stores, fp32 math. HBM-bound: it reads k*K and writes K elements per token.
 #include <algorithm>
 
 #include "common.hpp"
@@ -141,10 +140,114 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
   }
 }
 
+// One wavefront per token (rows of up to 4 * 64 chunks of 16 bytes), tokens strided over a grid
+// of a few blocks per CU: the whole of a token's k rows is loaded before any is used (16 chunks
+// per lane in flight), the norm's sum of squares is a wavefront reduction (no block barrier),
+// and the grid is not re-dispatched per token. Accumulation order as above: j ascending.
+template <typename T, bool NORM, int CH>
+__global__ __launch_bounds__(kThreads) void combine_wave_kernel(const T* __restrict__ y, const float* __restrict__ w,
+                                                                const float* __restrict__ g, T* __restrict__ out,
+                                                                int64_t ntok, int k, int K, float eps) {
+  constexpr int V = Vec16<T>::N;
+  constexpr int kBatch = 16 / CH;  // rows in flight
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  const int nch = K / V;
+  // the norm weights of this lane's columns, the same for every token
+  float gv[NORM ? CH : 1][V];
+#pragma unroll
+  for (int c = 0; c < (NORM ? CH : 1); ++c) {
+    const int ci = lane + c * kWave;
+#pragma unroll
+    for (int q = 0; q < V; ++q) gv[c][q] = (NORM && g && ci < nch) ? g[ci * V + q] : 1.f;
+  }
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + (threadIdx.x >> 6); t < ntok;
+       t += nwaves) {
+    float o[CH][V];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int q = 0; q < V; ++q) o[c][q] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      uint4 raw[kBatch][CH];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const T* yr = y + (t * k + min(j0 + u, k - 1)) * static_cast<int64_t>(K);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int ci = lane + c * kWave;
+          if (ci < nch) raw[u][c] = *reinterpret_cast<const uint4*>(yr + ci * V);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + u >= k) break;
+        const float wj = w[t * k + j0 + u];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int ci = lane + c * kWave;
+          if (ci < nch) {
+            float v[V];
+            Vec16<T>::load(reinterpret_cast<const T*>(&raw[u][c]), v);
+#pragma unroll
+            for (int q = 0; q < V; ++q) o[c][q] = fmaf(wj, v[q], o[c][q]);
+          }
+        }
+      }
+    }
+    float scale = 1.f;
+    if (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int ci = lane + c * kWave;
+        if (ci < nch) {
+#pragma unroll
+          for (int q = 0; q < V; ++q) ss = fmaf(o[c][q], o[c][q], ss);
+        }
+      }
+      ss = wave_sum(ss);
+      scale = 1.f / sqrtf(ss / static_cast<float>(K) + eps);
+    }
+    T* orow = out + t * static_cast<int64_t>(K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = lane + c * kWave;
+      if (ci < nch) {
+        float v[V];
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          float x = o[c][q];
+          if (NORM) {
+            x = x * scale;
+            if (g) x = x * gv[NORM ? c : 0][q];
+          }
+          v[q] = x;
+        }
+        Vec16<T>::store(orow + ci * V, v);
+      }
+    }
+  }
+}
+
 template <typename T, bool NORM>
 void launch_tn(const Layer& ly, const void* y, const float* w, const float* g, void* out, hipStream_t s) {
   const int K = static_cast<int>(ly.K);
   const int nch = K / Vec16<T>::N;
+  if (nch <= 4 * kWave && ly.T >= 2048) {
+    // wavefront per token (few tokens keep the block per token: more wavefronts in flight)
+    const int64_t blocks = std::min<int64_t>((ly.T + 3) / 4, static_cast<int64_t>(device_cu_count()) * 16);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const T* yy = static_cast<const T*>(y);
+    T* oo = static_cast<T*>(out);
+    if (nch <= kWave)
+      hipLaunchKernelGGL((combine_wave_kernel<T, NORM, 1>), grid, block, 0, s, yy, w, g, oo, ly.T, ly.k, K, ly.norm_eps);
+    else if (nch <= 2 * kWave)
+      hipLaunchKernelGGL((combine_wave_kernel<T, NORM, 2>), grid, block, 0, s, yy, w, g, oo, ly.T, ly.k, K, ly.norm_eps);
+    else
+      hipLaunchKernelGGL((combine_wave_kernel<T, NORM, 4>), grid, block, 0, s, yy, w, g, oo, ly.T, ly.k, K, ly.norm_eps);
+    return;
+  }
   const int nt = std::min(kThreads, ((nch + kWave - 1) / kWave) * kWave);
   const int ch = (nch + nt - 1) / nt;
   const dim3 grid(static_cast<unsigned>(ly.T)), block(static_cast<unsigned>(nt));

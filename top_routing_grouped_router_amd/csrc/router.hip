@@ -116,7 +116,8 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
     if (GATING == MOE_GATING_SIGMOID) {
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
-        float sc = 1.f / (1.f + expf(-v[i]));
+        // sigmoid = 1 / (1 + 2^(-v log2 e)) on the hardware exp2 and reciprocal (a few fp32 ulp)
+        float sc = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-v[i] * 1.44269504088896340736f));
         if (a.sig_eps != 0.f) sc = sc + a.sig_eps;
         s[i] = sc;
       }
@@ -158,45 +159,71 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
     code[i] = e < E ? key_code(key) : 0u;
   }
 
-  // k rounds. A lane's own best is its largest code, first slot on ties (lane l holds experts
-  // l, l+64, ..., so the first slot is its lowest index). The wave maximum code is found with
-  // DPP; usually one lane holds it and its best is the pick. When several lanes tie at the
-  // maximum, the lowest expert index among their bests wins. The pick's weight source (score,
-  // or logit for topk_softmax) comes from the owning lane's register by readlane.
+  // k rounds. Candidates are ordered by (code descending, expert index ascending); lane l
+  // holds experts l, l+64, ..., so inside a lane the slot order is the expert order. Each lane
+  // keeps its two greatest remaining candidates (b1 > b2, with their slots and weight sources)
+  // and a floor: its candidates at or above the floor are taken. A round finds the wave maximum
+  // of the lanes' b1 with DPP (usually one lane holds it; on a tie the lowest expert index among
+  // the tied lanes wins); the winning lane moves b2 up, or, when it had already used b2, re-scans
+  // its slots below the floor for a new pair. The rescan runs for one lane at most per round and
+  // only when that lane wins a second time, so a round is a few dozen instructions.
+  auto cand_val = [&](int i) __attribute__((always_inline)) { return (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[i] : s[i]; };
+  uint32_t b1 = 0, b2 = 0;
+  int s1 = 0, s2 = 0;
+  float v1 = 0.f, v2 = 0.f;
+  // top two of the slots whose (code, slot) lies below (fc, fs) (everything when !floor_set)
+  auto top2 = [&](bool floor_set, uint32_t fc, int fs) __attribute__((always_inline)) {
+    b1 = 0; b2 = 0; s1 = 0; s2 = 0; v1 = 0.f; v2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      uint32_t c = code[i];
+      if (floor_set && !(c < fc || (c == fc && i > fs))) c = 0;
+      const float cv = cand_val(i);
+      // branch-free, so the pairs stay in registers
+      const bool gt1 = c > b1, gt2 = c > b2;
+      b2 = gt1 ? b1 : (gt2 ? c : b2);
+      s2 = gt1 ? s1 : (gt2 ? i : s2);
+      v2 = gt1 ? v1 : (gt2 ? cv : v2);
+      b1 = gt1 ? c : b1;
+      s1 = gt1 ? i : s1;
+      v1 = gt1 ? cv : v1;
+    }
+  };
+  top2(false, 0u, 0);
+  bool have2 = true;
   int my_sel = 0;
   float my_val = 0.f;
   for (int j = 0; j < a.k; ++j) {
-    uint32_t best = 0;
-    int bslot = 0;
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-      if (code[i] > best) {
-        best = code[i];
-        bslot = i;
-      }
-    float bval = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[0] : s[0];
-#pragma unroll
-    for (int i = 1; i < PL; ++i)
-      if (bslot == i) bval = (GATING == MOE_GATING_TOPK_SOFTMAX) ? v[i] : s[i];
-    const uint32_t m = wave_max_u32_dpp(best);
-    const uint64_t ball = __ballot(best == m);
+    const uint32_t m = wave_max_u32_dpp(b1);
+    const uint64_t ball = __ballot(b1 == m);
     int e;
     if (__popcll(ball) == 1) {
       const int wl = __ffsll(static_cast<unsigned long long>(ball)) - 1;
-      e = __builtin_amdgcn_readlane(bslot, wl) * kWave + wl;
+      e = __builtin_amdgcn_readlane(s1, wl) * kWave + wl;
     } else {
-      e = wave_min_i32_dpp(best == m ? bslot * kWave + lane : 0x7fffffff);
+      e = wave_min_i32_dpp(b1 == m ? s1 * kWave + lane : 0x7fffffff);
     }
     e = min(max(e, 0), E - 1);  // k <= E, so a candidate always exists
-    const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bval), e & (kWave - 1)));
+    const int wl = e & (kWave - 1);
+    const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v1), wl));
     if (lane == j) {
       my_sel = e;
       my_val = val;
     }
-    if (lane == (e & (kWave - 1))) {
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (i == (e >> 6)) code[i] = 0;
+    // whether the winner still holds its second candidate: uniform, so the rescan is a
+    // wave-level branch taken only when needed
+    if (__builtin_amdgcn_readlane(have2 ? 1 : 0, wl) != 0) {
+      if (lane == wl) {
+        b1 = b2; s1 = s2; v1 = v2;
+        have2 = false;
+      }
+    } else {
+      const uint32_t fc = b1;
+      const int fs = s1;
+      if (lane == wl) {
+        top2(true, fc, fs);
+        have2 = true;
+      }
     }
   }
 
