@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the extra measurement of the routed experts' backward")
     ap.add_argument("--stages", action="store_true", help="also time each stage call alone")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the measurement of the achievable matrix-core and copy rates")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference the HBM "
                          "byte counters are scaled by")
@@ -171,6 +173,27 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def calibration(moe, torch):
+    """Achievable bf16 matrix-core rate (TFLOP/s) and HBM copy rate (GB/s of read + write) of
+    this device, each the median of 5 event-timed launches of the library's calibration kernels."""
+    out, flops = moe.calibrate_mfma_bf16(200)
+    t = event_time_ms(lambda: moe.calibrate_mfma_bf16(200, out), 3, torch)
+    iters = max(200, int(200 * 3.0 / max(t, 1e-3)))  # about 3 ms per launch
+    moe.calibrate_mfma_bf16(iters, out)
+    ts = sorted(event_time_ms(lambda: moe.calibrate_mfma_bf16(iters, out), 1, torch) for _ in range(5))
+    flops = moe.calibrate_mfma_bf16(iters, out)[1]
+    mfma = flops / (ts[2] / 1e3) / 1e12
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    moe.calibrate_copy(src, dst)
+    cs = sorted(event_time_ms(lambda: moe.calibrate_copy(src, dst), 1, torch) for _ in range(5))
+    del src, dst
+    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_loop_iters": iters, "mfma_loop_ms": round(ts[2], 4),
+            "copy_gbs": round(2 * nbytes / (cs[2] / 1e3) / 1e9, 1), "copy_bytes": nbytes,
+            "copy_ms": round(cs[2], 4)}
 
 
 def cpu_baseline(cfg, w, x, n_tokens):
@@ -340,6 +363,14 @@ def main():
             n = torch.empty((T, L), dtype=x.dtype, device=x.device)
             st["latent_up"] = event_time_ms(lambda: moe.latent_up(cfg, w, n), 5, torch)
         out["stages_ms"] = {k2: round(v, 4) for k2, v in st.items()}
+    if not args.no_calibration:
+        # Rates this device achieves (the published peaks assume clocks the chip does not hold
+        # under sustained matrix load): the library's register-only matrix-core loop and its
+        # 16-byte-vector copy, timed with HIP events on the current stream.
+        cal = calibration(moe, torch)
+        out["calibration"] = cal
+        out["roofline"]["achievable_peak"] = cal["mfma_bf16_tflops"]
+        out["roofline"]["frac_of_achievable"] = round(achieved / cal["mfma_bf16_tflops"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_tokens)
     print(json.dumps(out), flush=True)

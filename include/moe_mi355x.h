@@ -47,7 +47,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
 
@@ -406,6 +406,28 @@ MOE_API moe_status_t moe_load_imbalance(int32_t num_experts, const int64_t* coun
  * a non-finite bias_gamma. */
 MOE_API moe_status_t moe_score_bias_update(int32_t num_experts, float bias_gamma, int64_t* accumulator,
                                            float* score_bias, double* imbalance, void* stream);
+
+/* ------------------------------------------------------------------------ calibration */
+
+/*
+ * Measurement support, not part of the layer: the rates this device achieves, which the layer's
+ * kernels are reported against beside the published peaks.
+ *
+ * moe_calibrate_mfma_bf16: one workgroup of 8 wavefronts per compute unit, each wavefront running
+ * `iters` rounds of 8 independent 32x32x16 bf16 matrix-core products (fp32 accumulation) on
+ * register operands, with no memory traffic. *num_waves receives the number of wavefronts and
+ * *flops the launch's dense flop count (2*32*32*16 per product); the caller times the stream.
+ * Each wavefront writes one float (a sum of its accumulators) to out[wave], so out (device, fp32)
+ * must hold *num_waves values. out == NULL only fills *num_waves and *flops and enqueues nothing.
+ * INVALID_ARG for iters < 1 or NULL num_waves / flops.
+ *
+ * moe_calibrate_copy: copies `bytes` (a positive multiple of 16) from src to dst (device, 16-byte
+ * aligned, not overlapping) with 16-byte vector loads and stores; HBM traffic 2 * bytes.
+ * INVALID_ARG for NULL pointers or a bad size.
+ */
+MOE_API moe_status_t moe_calibrate_mfma_bf16(int64_t iters, float* out, int64_t* num_waves, double* flops,
+                                             void* stream);
+MOE_API moe_status_t moe_calibrate_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,8 @@ def test_header_declares_the_abi():
                  "moe_workspace_size", "moe_status_string", "moe_last_error_message",
                  "moe_abi_version", "moe_accumulate_expert_counts", "moe_load_imbalance",
                  "moe_score_bias_update", "moe_expert_capacity", "moe_experts_forward_train",
-                 "moe_experts_backward", "moe_experts_backward_workspace_size", "moe_combine_backward"):
+                 "moe_experts_backward", "moe_experts_backward_workspace_size", "moe_combine_backward",
+                 "moe_calibrate_mfma_bf16", "moe_calibrate_copy"):
         assert name in syms
 
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_size():
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
     c = moe._CConfig()
     assert moe._config_default(ctypes.byref(c)) == 0
     assert c.struct_size == ctypes.sizeof(moe._CConfig)
@@ -236,3 +237,16 @@ def test_backward_entry_points_validate_before_any_gpu_call():
     assert moe._combine_backward(ctypes.byref(c), 0, None, None, None, None, None, None) == 0
     assert moe._experts_backward(ctypes.byref(c), ctypes.byref(w), 0, *([None] * 7), None, None, None, 0,
                                  None) == 1
+
+
+def test_calibration_entry_points_validate_before_any_gpu_call():
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    waves, flops = ctypes.c_int64(0), ctypes.c_double(0.0)
+    assert moe._calibrate_mfma(0, fake, ctypes.byref(waves), ctypes.byref(flops), None) == 1
+    assert "iters" in moe._last_error().decode()
+    assert moe._calibrate_mfma(10, fake, None, ctypes.byref(flops), None) == 1
+    assert moe._calibrate_mfma(10, fake, ctypes.byref(waves), None, None) == 1
+    for nbytes in (0, -16, 24):
+        assert moe._calibrate_copy(fake, fake, nbytes, None) == 1
+    assert moe._calibrate_copy(None, fake, 64, None) == 1
+    assert moe._calibrate_copy(fake, None, 64, None) == 1

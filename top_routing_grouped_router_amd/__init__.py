@@ -105,6 +105,8 @@ _mx_quantize = _sig("moe_mx_quantize", c_i32, c_i64, c_i64, c_vp, c_vp, c_vp, c_
 _accumulate_counts = _sig("moe_accumulate_expert_counts", c_i32, c_i32, c_vp, c_vp, c_vp)
 _load_imbalance = _sig("moe_load_imbalance", c_i32, c_i32, c_vp, c_vp, c_vp)
 _score_bias_update = _sig("moe_score_bias_update", c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp)
+_calibrate_mfma = _sig("moe_calibrate_mfma_bf16", c_i32, c_i64, c_vp, c_vp, c_vp, c_vp)
+_calibrate_copy = _sig("moe_calibrate_copy", c_i32, c_vp, c_vp, c_i64, c_vp)
 
 
 class MoEError(RuntimeError):
@@ -558,3 +560,27 @@ def mx_quantize(x: torch.Tensor):
     scales = torch.empty((*x.shape[:-1], cols // 32), dtype=torch.uint8, device=x.device)
     _check(_mx_quantize(rows, cols, _ptr(x.contiguous()), _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
+
+
+# --------------------------------------------------------------------------- calibration
+
+def calibrate_mfma_bf16(iters: int, out: Optional[torch.Tensor] = None):
+    """Enqueue the matrix-core loop (measurement support, not part of the layer): every
+    wavefront runs `iters` rounds of 8 register-only 32x32x16 bf16 products. Returns (out, flops)
+    with out the per-wavefront sums (float32 on the current device) and flops the launch's dense
+    flop count; time the current stream around this call."""
+    waves, flops = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(_calibrate_mfma(iters, None, ctypes.byref(waves), ctypes.byref(flops), _stream()))
+    if out is None:
+        out = torch.empty(waves.value, dtype=torch.float32, device="cuda")
+    _expect(out, (waves.value,), torch.float32, "out")
+    _check(_calibrate_mfma(iters, _ptr(out), ctypes.byref(waves), ctypes.byref(flops), _stream()))
+    return out, flops.value
+
+
+def calibrate_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Enqueue a 16-byte-vector device copy of src's bytes into dst (measurement support)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(_calibrate_copy(_ptr(src), _ptr(dst), nbytes, _stream()))
