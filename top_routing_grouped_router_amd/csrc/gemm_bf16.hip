@@ -392,6 +392,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       const int i = wave + S::NW * q;
       if (S::NI % S::NW != 0 && i >= S::NI) continue;
       const bool is_a = load_is_a(q);
+      // Small tiles (few rows per expert): token rows past the tile's last valid row are never
+      // stored, so their loads are skipped (whatever LDS holds there only feeds output rows
+      // that are dropped). The large tiles keep every load: the extra live register spills.
+      if (S::BM < 256 && !TA && !WGRAD && is_a && i * S::kRowsPerDma >= t.rows) continue;
       const unsigned char* g = (is_a ? (WGRAD ? t.Abase : Ab) : t.Bexp) +
                                (t.src_off[q] + static_cast<uint32_t>(kt) * (is_a ? a_step : b_step));
       if (WGRAD) {
@@ -585,6 +589,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       wait_lgkmcnt0();
       __builtin_amdgcn_s_barrier();
+      // The scatter indices of this round (loaded at its start) are waited for once here; left
+      // to the compiler, every store would wait for all vector-memory operations in flight
+      // (the next tile's first loads and the previous stores) before using its index.
+      if constexpr (SCATTER) wait_vmcnt<0>();
       // The accumulators are dead once the last round is in LDS: set up the next tile then
       // (its index loads, then its first DMA loads, ahead of this round's stores).
       const int cc = tid % CPR;
