@@ -141,7 +141,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
 }
 
 // One wavefront per token (rows of up to 4 * 64 chunks of 16 bytes), tokens strided over a grid
-// of a few blocks per CU: the whole of a token's k rows is loaded before any is used (16 chunks
+// of 4 blocks per CU (measured against 1, 2, 8, 16 and 32: fewer, longer-lived wavefronts;
+// latent896 -12 % against 16): the whole of a token's k rows is loaded before any is used (16 chunks
 // per lane in flight), the norm's sum of squares is a wavefront reduction (no block barrier),
 // and the grid is not re-dispatched per token. Accumulation order as above: j ascending.
 template <typename T, bool NORM, int CH>
@@ -236,7 +237,7 @@ void launch_tn(const Layer& ly, const void* y, const float* w, const float* g, v
   const int nch = K / Vec16<T>::N;
   if (nch <= 4 * kWave && ly.T >= 2048) {
     // wavefront per token (few tokens keep the block per token: more wavefronts in flight)
-    const int64_t blocks = std::min<int64_t>((ly.T + 3) / 4, static_cast<int64_t>(device_cu_count()) * 16);
+    const int64_t blocks = std::min<int64_t>((ly.T + 3) / 4, static_cast<int64_t>(device_cu_count()) * 4);
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     const T* yy = static_cast<const T*>(y);
     T* oo = static_cast<T*>(out);
