@@ -211,8 +211,16 @@ def test_experts_forward(case):
                                   ("latent896", 300, dict(d_model=512, latent_dim=256, num_experts=32)),
                                   ("tiny_f32", None, {}),
                                   ("latent896", 100, dict(d_model=512, latent_dim=256, num_experts=32,
-                                                          dtype="f32"))],
-                         ids=lambda c: f"{c[0]}-{c[2].get('dtype', '')}")
+                                                          dtype="f32")),
+                                  # from 2048 tokens on: one wavefront per token over a strided grid,
+                                  # rows of 1, 2 and 4 x 64 chunks, ragged token counts
+                                  ("olmoe", 2501, dict(d_model=512, num_experts=16, top_k=4, hidden_size=128)),
+                                  ("olmoe", 2049, dict(d_model=2048, num_experts=16, top_k=4, hidden_size=128)),
+                                  ("latent896", 2050, dict(d_model=512, latent_dim=256, num_experts=32)),
+                                  ("latent896", 2303, dict(d_model=1024, latent_dim=1024, num_experts=32)),
+                                  ("latent896", 2100, dict(d_model=512, latent_dim=256, num_experts=32,
+                                                           dtype="f32"))],
+                         ids=lambda c: f"{c[0]}-{c[1]}-{c[2].get('dtype', '')}")
 def test_combine(case):
     name, T, over = case
     banner(f"combine {case}")
