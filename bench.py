@@ -176,22 +176,28 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
 
 
 def calibration(moe, torch):
-    """Achievable bf16 matrix-core rate (TFLOP/s) and HBM copy rate (GB/s of read + write) of
-    this device, each the median of 5 event-timed launches of the library's calibration kernels."""
-    out, flops = moe.calibrate_mfma_bf16(200)
-    t = event_time_ms(lambda: moe.calibrate_mfma_bf16(200, out), 3, torch)
-    iters = max(200, int(200 * 3.0 / max(t, 1e-3)))  # about 3 ms per launch
-    moe.calibrate_mfma_bf16(iters, out)
-    ts = sorted(event_time_ms(lambda: moe.calibrate_mfma_bf16(iters, out), 1, torch) for _ in range(5))
-    flops = moe.calibrate_mfma_bf16(iters, out)[1]
-    mfma = flops / (ts[2] / 1e3) / 1e12
+    """Achievable matrix-core rates (TFLOP/s: bf16, and the block-scaled FP8 of the MXFP8 experts)
+    and HBM copy rate (GB/s of read + write) of this device, each the median of 5 event-timed
+    launches of the library's calibration kernels (about 3 ms each)."""
+    def loop_rate(run):
+        out, _ = run(200)
+        t = event_time_ms(lambda: run(200, out), 3, torch)
+        iters = max(200, int(200 * 3.0 / max(t, 1e-3)))
+        run(iters, out)
+        ts = sorted(event_time_ms(lambda: run(iters, out), 1, torch) for _ in range(5))
+        return run(iters, out)[1] / (ts[2] / 1e3) / 1e12, iters, ts[2]
+
+    bf16, iters, ms = loop_rate(moe.calibrate_mfma_bf16)
+    mx, mx_iters, mx_ms = loop_rate(moe.calibrate_mfma_mxfp8)
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     moe.calibrate_copy(src, dst)
     cs = sorted(event_time_ms(lambda: moe.calibrate_copy(src, dst), 1, torch) for _ in range(5))
     del src, dst
-    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_loop_iters": iters, "mfma_loop_ms": round(ts[2], 4),
+    return {"mfma_bf16_tflops": round(bf16, 1), "mfma_loop_iters": iters, "mfma_loop_ms": round(ms, 4),
+            "mfma_mxfp8_tflops": round(mx, 1), "mfma_mxfp8_loop_iters": mx_iters,
+            "mfma_mxfp8_loop_ms": round(mx_ms, 4),
             "copy_gbs": round(2 * nbytes / (cs[2] / 1e3) / 1e9, 1), "copy_bytes": nbytes,
             "copy_ms": round(cs[2], 4)}
 
@@ -371,6 +377,10 @@ def main():
         out["calibration"] = cal
         out["roofline"]["achievable_peak"] = cal["mfma_bf16_tflops"]
         out["roofline"]["frac_of_achievable"] = round(achieved / cal["mfma_bf16_tflops"], 4)
+        if "mxfp8_experts" in out:
+            mxr = out["mxfp8_experts"]
+            mxr["achievable_peak_tflops"] = cal["mfma_mxfp8_tflops"]
+            mxr["frac_of_achievable"] = round(mxr["achieved_tflops"] / cal["mfma_mxfp8_tflops"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_tokens)
     print(json.dumps(out), flush=True)

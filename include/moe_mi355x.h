@@ -47,7 +47,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
 
@@ -427,6 +427,10 @@ MOE_API moe_status_t moe_score_bias_update(int32_t num_experts, float bias_gamma
  */
 MOE_API moe_status_t moe_calibrate_mfma_bf16(int64_t iters, float* out, int64_t* num_waves, double* flops,
                                              void* stream);
+/* The same for the block-scaled FP8 products of the MXFP8 expert matmuls: rounds of 8 independent
+ * 32x32x64 E4M3 products with unit E8M0 scales (2*32*32*64 flops each); same arguments. */
+MOE_API moe_status_t moe_calibrate_mfma_mxfp8(int64_t iters, float* out, int64_t* num_waves, double* flops,
+                                              void* stream);
 MOE_API moe_status_t moe_calibrate_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus

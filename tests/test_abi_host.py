@@ -32,7 +32,7 @@ def test_header_declares_the_abi():
                  "moe_abi_version", "moe_accumulate_expert_counts", "moe_load_imbalance",
                  "moe_score_bias_update", "moe_expert_capacity", "moe_experts_forward_train",
                  "moe_experts_backward", "moe_experts_backward_workspace_size", "moe_combine_backward",
-                 "moe_calibrate_mfma_bf16", "moe_calibrate_copy"):
+                 "moe_calibrate_mfma_bf16", "moe_calibrate_mfma_mxfp8", "moe_calibrate_copy"):
         assert name in syms
 
 
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_size():
-    assert moe.abi_version() == 5
+    assert moe.abi_version() == 6
     c = moe._CConfig()
     assert moe._config_default(ctypes.byref(c)) == 0
     assert c.struct_size == ctypes.sizeof(moe._CConfig)
@@ -246,6 +246,8 @@ def test_calibration_entry_points_validate_before_any_gpu_call():
     assert "iters" in moe._last_error().decode()
     assert moe._calibrate_mfma(10, fake, None, ctypes.byref(flops), None) == 1
     assert moe._calibrate_mfma(10, fake, ctypes.byref(waves), None, None) == 1
+    assert moe._calibrate_mfma_mx(0, fake, ctypes.byref(waves), ctypes.byref(flops), None) == 1
+    assert moe._calibrate_mfma_mx(10, fake, None, ctypes.byref(flops), None) == 1
     for nbytes in (0, -16, 24):
         assert moe._calibrate_copy(fake, fake, nbytes, None) == 1
     assert moe._calibrate_copy(None, fake, 64, None) == 1

@@ -21,18 +21,20 @@ def banner(msg):
     print(f"[case] {msg}", flush=True)
 
 
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
 @pytest.mark.parametrize("iters", [1, 37, 400])
-def test_mfma_loop(iters):
-    banner(f"mfma loop iters={iters}")
-    out, flops = moe.calibrate_mfma_bf16(iters)
+def test_mfma_loop(iters, mx):
+    banner(f"mfma loop iters={iters} mx={mx}")
+    run = moe.calibrate_mfma_mxfp8 if mx else moe.calibrate_mfma_bf16
+    out, flops = run(iters)
     torch.cuda.synchronize()
     waves = out.numel()
     assert waves == torch.cuda.get_device_properties(0).multi_processor_count * 8
-    assert flops == waves * iters * 8 * 2 * 32 * 32 * 16
+    assert flops == waves * iters * 8 * 2 * 32 * 32 * (64 if mx else 16)
     assert torch.isfinite(out).all()
     # the operands are fixed per lane, so every round adds the same products: the sums grow
     # linearly with the rounds (up to fp32 rounding)
-    out2, _ = moe.calibrate_mfma_bf16(2 * iters)
+    out2, _ = run(2 * iters)
     torch.cuda.synchronize()
     assert torch.allclose(out2, 2 * out, rtol=1e-3, atol=1e-3 * float(out.abs().max()))
     assert float(out.abs().max()) > 0

@@ -106,6 +106,7 @@ _accumulate_counts = _sig("moe_accumulate_expert_counts", c_i32, c_i32, c_vp, c_
 _load_imbalance = _sig("moe_load_imbalance", c_i32, c_i32, c_vp, c_vp, c_vp)
 _score_bias_update = _sig("moe_score_bias_update", c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp)
 _calibrate_mfma = _sig("moe_calibrate_mfma_bf16", c_i32, c_i64, c_vp, c_vp, c_vp, c_vp)
+_calibrate_mfma_mx = _sig("moe_calibrate_mfma_mxfp8", c_i32, c_i64, c_vp, c_vp, c_vp, c_vp)
 _calibrate_copy = _sig("moe_calibrate_copy", c_i32, c_vp, c_vp, c_i64, c_vp)
 
 
@@ -564,18 +565,27 @@ def mx_quantize(x: torch.Tensor):
 
 # --------------------------------------------------------------------------- calibration
 
+def _calibrate(fn, iters, out):
+    waves, flops = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(fn(iters, None, ctypes.byref(waves), ctypes.byref(flops), _stream()))
+    if out is None:
+        out = torch.empty(waves.value, dtype=torch.float32, device="cuda")
+    _expect(out, (waves.value,), torch.float32, "out")
+    _check(fn(iters, _ptr(out), ctypes.byref(waves), ctypes.byref(flops), _stream()))
+    return out, flops.value
+
+
 def calibrate_mfma_bf16(iters: int, out: Optional[torch.Tensor] = None):
     """Enqueue the matrix-core loop (measurement support, not part of the layer): every
     wavefront runs `iters` rounds of 8 register-only 32x32x16 bf16 products. Returns (out, flops)
     with out the per-wavefront sums (float32 on the current device) and flops the launch's dense
     flop count; time the current stream around this call."""
-    waves, flops = ctypes.c_int64(0), ctypes.c_double(0.0)
-    _check(_calibrate_mfma(iters, None, ctypes.byref(waves), ctypes.byref(flops), _stream()))
-    if out is None:
-        out = torch.empty(waves.value, dtype=torch.float32, device="cuda")
-    _expect(out, (waves.value,), torch.float32, "out")
-    _check(_calibrate_mfma(iters, _ptr(out), ctypes.byref(waves), ctypes.byref(flops), _stream()))
-    return out, flops.value
+    return _calibrate(_calibrate_mfma, iters, out)
+
+
+def calibrate_mfma_mxfp8(iters: int, out: Optional[torch.Tensor] = None):
+    """The same loop on 32x32x64 block-scaled E4M3 products (the MXFP8 expert matmuls')."""
+    return _calibrate(_calibrate_mfma_mx, iters, out)
 
 
 def calibrate_copy(src: torch.Tensor, dst: torch.Tensor) -> None:

@@ -1058,22 +1058,33 @@ namespace moe {
 // csrc/calibrate.hip: the matrix-core loop (one float per wavefront to `out`, mfma_loop_waves()
 // of them; mfma_loop_flops(iters) dense flops per launch) and a plain 16-byte-vector copy.
 int64_t mfma_loop_waves();
-double mfma_loop_flops(int64_t iters);
-hipError_t launch_mfma_loop(float* out, int64_t iters, hipStream_t s);
+double mfma_loop_flops(int64_t iters, bool mx);
+hipError_t launch_mfma_loop(float* out, int64_t iters, bool mx, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 }  // namespace moe
 
-extern "C" moe_status_t moe_calibrate_mfma_bf16(int64_t iters, float* out, int64_t* num_waves, double* flops,
-                                                void* stream) {
+namespace {
+moe_status_t calibrate_mfma(int64_t iters, float* out, int64_t* num_waves, double* flops, bool mx, void* stream) {
   if (iters < 1) return fail(MOE_ERR_INVALID_ARG, "iters must be >= 1");
   moe_status_t st;
   if ((st = need(num_waves, "num_waves")) != MOE_OK) return st;
   if ((st = need(flops, "flops")) != MOE_OK) return st;
   *num_waves = mfma_loop_waves();
-  *flops = mfma_loop_flops(iters);
+  *flops = mfma_loop_flops(iters, mx);
   if (!out) return ok();
-  MOE_TRY_HIP(launch_mfma_loop(out, iters, static_cast<hipStream_t>(stream)), "mfma loop");
+  MOE_TRY_HIP(launch_mfma_loop(out, iters, mx, static_cast<hipStream_t>(stream)), "mfma loop");
   return ok();
+}
+}  // namespace
+
+extern "C" moe_status_t moe_calibrate_mfma_bf16(int64_t iters, float* out, int64_t* num_waves, double* flops,
+                                                void* stream) {
+  return calibrate_mfma(iters, out, num_waves, flops, false, stream);
+}
+
+extern "C" moe_status_t moe_calibrate_mfma_mxfp8(int64_t iters, float* out, int64_t* num_waves, double* flops,
+                                                 void* stream) {
+  return calibrate_mfma(iters, out, num_waves, flops, true, stream);
 }
 
 extern "C" moe_status_t moe_calibrate_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -9,6 +9,8 @@
 //     and the loop then runs at the published 2.4 GHz peak, which real data does not). Operands
 //     are not modified inside the loop: rewriting registers that in-flight MFMAs still read
 //     stalls the matrix pipe (a rotating variant measured 1.23 PFLOP/s against 1.97).
+//   * mfma_mx_loop_kernel: the same loop on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands,
+//     unit block scales), the product the MXFP8 expert GEMMs run.
 //   * copy_kernel: a grid-stride copy, 4 non-temporal 16-byte loads in flight per thread before
 //     the stores (one load per thread measured 5.0 TB/s, four 6.0 TB/s of read + write traffic;
 //     torch's device copy 5.1 TB/s).
@@ -54,6 +56,45 @@ __global__ __launch_bounds__(kLoopWaves * kWave) __attribute__((amdgpu_waves_per
   if (lane == 0) out[static_cast<int64_t>(blockIdx.x) * kLoopWaves + threadIdx.x / kWave] = s;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The same loop on the block-scaled FP8 products the MXFP8 expert GEMMs use
+// (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 operands, unit E8M0 scales).
+__global__ __launch_bounds__(kLoopWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void mfma_mx_loop_kernel(
+    float* __restrict__ out, int64_t iters) {
+  const int lane = threadIdx.x & (kWave - 1);
+  i32x8 ra, rb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // four E4M3 codes per dword, each of magnitude in [2^-3, 2^1): exponent field 4..7
+    uint32_t wa = 0, wb = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int u = (lane * 29 + i * 7 + b * 3 + threadIdx.x / kWave) & 63;
+      wa |= static_cast<uint32_t>(((u & 1) << 7) | ((4 + (u >> 4) % 4) << 3) | (u & 7)) << (8 * b);
+      wb |= static_cast<uint32_t>((((u >> 1) & 1) << 7) | ((4 + (u >> 3) % 4) << 3) | ((u * 5) & 7)) << (8 * b);
+    }
+    ra[i] = static_cast<int>(wa);
+    rb[i] = static_cast<int>(wb);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ra, rb, acc[j], 0, 0, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  if (lane == 0) out[static_cast<int64_t>(blockIdx.x) * kLoopWaves + threadIdx.x / kWave] = s;
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCopyUnroll = 4;
@@ -76,13 +117,17 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
 
 int64_t mfma_loop_waves() { return static_cast<int64_t>(device_cu_count()) * kLoopWaves; }
 
-double mfma_loop_flops(int64_t iters) {
-  return static_cast<double>(mfma_loop_waves()) * static_cast<double>(iters) * 8.0 * (2.0 * 32 * 32 * 16);
+double mfma_loop_flops(int64_t iters, bool mx) {
+  return static_cast<double>(mfma_loop_waves()) * static_cast<double>(iters) * 8.0 *
+         (mx ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);
 }
 
-hipError_t launch_mfma_loop(float* out, int64_t iters, hipStream_t s) {
-  hipLaunchKernelGGL(mfma_loop_kernel, dim3(static_cast<unsigned>(device_cu_count())), dim3(kLoopWaves * kWave), 0, s,
-                     out, iters);
+hipError_t launch_mfma_loop(float* out, int64_t iters, bool mx, hipStream_t s) {
+  const dim3 g(static_cast<unsigned>(device_cu_count())), b(kLoopWaves * kWave);
+  if (mx)
+    hipLaunchKernelGGL(mfma_mx_loop_kernel, g, b, 0, s, out, iters);
+  else
+    hipLaunchKernelGGL(mfma_loop_kernel, g, b, 0, s, out, iters);
   return hipGetLastError();
 }
 
