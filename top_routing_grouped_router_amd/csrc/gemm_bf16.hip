@@ -48,7 +48,8 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 
-template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_, int PLANES_ = 1, int EB_ = 2>
+template <int WM_, int WN_, int TM_, int TN_, int BK_, int NSTAGE_, int WG_PER_CU_, int PLANES_ = 1, int EB_ = 2,
+          int SCG_ = 1>
 struct Shape {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
   // Bytes per operand element: 2 = bf16; 1 = MXFP8 (E4M3 codes with one E8M0 scale byte per
@@ -74,14 +75,20 @@ struct Shape {
   static constexpr int NQ = (NI + NW - 1) / NW;        // per wavefront (upper bound)
   static constexpr int NQMIN = NI / NW;                // per wavefront (lower bound)
   static constexpr int DATA = (BM + BROWS) * ROWB;  // operand bytes per stage
-  // MXFP8: the stage's scale bytes follow the operands, 4 per staged row (k-stage 128 = four
-  // blocks of 32); one 4-byte-per-lane DMA load per 64 rows.
+  // MXFP8 scales: 4 bytes per staged row and k-stage (k-stage 128 = four blocks of 32), one
+  // DMA load per 64 rows. SCG = 1: each stage's scale bytes follow its operands (4 bytes per
+  // lane). SCG = 4: the scales of four consecutive k-stages travel together (16 bytes per lane,
+  // issued with every fourth stage, a quarter of the line requests) into a two-group area
+  // after the ring: group g serves stages 4g..4g+3 from half g % 2.
+  static constexpr int SCG = MX ? SCG_ : 0;
   static constexpr int SCB = MX ? BK / 32 : 0;
   static constexpr int NSC = MX ? (BM + BROWS) / 64 : 0;
-  static constexpr int STAGE = DATA + (BM + BROWS) * SCB;
-  static constexpr int LDS = NSTAGE * STAGE;
+  static constexpr int STAGE = DATA + (SCG == 1 ? (BM + BROWS) * SCB : 0);
+  static constexpr int SCHALF = SCG == 4 ? (BM + BROWS) * 16 : 0;  // bytes per scale group
+  static constexpr int LDS = NSTAGE * STAGE + 2 * SCHALF;
   static_assert(!MX || (BK == 128 && PLANES == 1 && BM % 64 == 0 && BN % 64 == 0 && NSC <= NW),
                 "MXFP8 stages: 128-element k-stages, 64-row scale loads, one per wavefront");
+  static_assert(!MX || SCG == 1 || SCG == 4, "scale groups of one or four k-stages");
   static_assert(BM % kRowsPerDma == 0 && BN % kRowsPerDma == 0, "whole DMA loads per tile");
   static_assert(BK % 16 == 0 && CHUNKS >= 2 && CHUNKS <= 8, "stage depth");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "vmcnt bookkeeping covers 2..4 stages");
@@ -99,6 +106,9 @@ using ShapeSmall = Shape<1, 4, 2, 2, 64, 2, 2>;
 // MXFP8 expert GEMMs: the large tile with 128-element k-stages (one 128-byte line of E4M3 codes
 // per row) plus the rows' scale bytes; 2 stages x 66 KiB.
 using ShapeLargeMX = Shape<2, 4, 4, 2, 128, 2, 1, 1, 1>;
+// The same with the scales of four k-stages per load (k a multiple of 512): 2 stages x 64 KiB
+// plus 2 x 8 KiB of scale groups.
+using ShapeLargeMXG = Shape<2, 4, 4, 2, 128, 2, 1, 1, 1, 4>;
 // Router logits: 256 tokens x 128 experts x 3 weight planes, 8 wavefronts (2 x 4) of 128 x 32;
 // 2 stages x 80 KiB (the whole LDS).
 using ShapeRouter = Shape<2, 4, 4, 1, 64, 2, 1, 3>;
@@ -406,10 +416,17 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       }
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
     }
-    if constexpr (S::MX) {
+    if constexpr (S::SCG == 1) {
       if (wave < S::NSC)
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(t.sc_base + (t.sc_off + static_cast<uint32_t>(kt) * 4)),
                                          LDS_PTR(st + S::DATA + wave * 256), 4, 0, 0);
+    } else if constexpr (S::SCG == 4) {
+      // Stage kt's loads land before stage kt runs; group kt / 4 goes to the half that group
+      // kt / 4 - 2 used, whose last reader (stage kt - 5) every wavefront has passed.
+      if (wave < S::NSC && (kt & 3) == 0)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(t.sc_base + (t.sc_off + static_cast<uint32_t>(kt) * 4)),
+                                         LDS_PTR(lds + S::NSTAGE * S::STAGE + ((kt >> 2) & 1) * S::SCHALF + wave * 1024),
+                                         16, 0, 0);
     }
   };
 
@@ -440,14 +457,15 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   };
   // scale bytes [b0 b1 b2 b3] of the stage's four blocks, shifted so that byte 0 is block
   // (lane / 32) (64-k step 0) and byte 2 block 2 + (lane / 32) (step 1)
-  auto lds_scales = [&](const unsigned char* scl) {
+  // (scl: the stage's scale words, rstride bytes apart per staged row)
+  auto lds_scales = [&](const unsigned char* scl, int rstride) {
     const int shift = 8 * (lane >> 5);
 #pragma unroll
     for (int j = 0; j < S::TN; ++j)
-      scw[j] = *reinterpret_cast<const uint32_t*>(scl + (S::BM + wn * S::TN * 32 + j * 32 + (lane & 31)) * 4) >> shift;
+      scw[j] = *reinterpret_cast<const uint32_t*>(scl + (S::BM + wn * S::TN * 32 + j * 32 + (lane & 31)) * rstride) >> shift;
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
-      sct[i] = *reinterpret_cast<const uint32_t*>(scl + (wm * S::TM * 32 + i * 32 + (lane & 31)) * 4) >> shift;
+      sct[i] = *reinterpret_cast<const uint32_t*>(scl + (wm * S::TM * 32 + i * 32 + (lane & 31)) * rstride) >> shift;
   };
   auto lds_frags = [&](int fs, const unsigned char* la, const unsigned char* lb, int kk) {
     const int ch = 2 * kk + (lane >> 5);
@@ -718,7 +736,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // trip before every MFMA group.
       if constexpr (S::MX) {
         // two 64-k steps per 128-element stage; scale words read once per stage
-        lds_scales(la + S::DATA);
+        if constexpr (S::SCG == 1)
+          lds_scales(la + S::DATA, 4);
+        else
+          lds_scales(lds + S::NSTAGE * S::STAGE + ((kt >> 2) & 1) * S::SCHALF + (kt & 3) * 4, 16);
         lds_frags_mx(0, la, lb, 0);
 #pragma unroll
         for (int kk = 0; kk < S::BK / 64; ++kk) {
@@ -833,12 +854,11 @@ int gemm_bf16_pick_variant(double mean_rows_per_group) { return mean_rows_per_gr
 
 int gemm_mx_tile_m() { return ShapeLargeMX::BM; }
 
-hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s) {
-  if (c.dense_M > 0 || c.Kd % ShapeLargeMX::BK != 0 || !c.a_scale || !c.b_scale) return hipErrorInvalidValue;
+template <class S>
+hipError_t launch_mx_shape(const GemmCall& c, hipStream_t s) {
   if (c.c_codes) {
     // SwiGLU GEMM with an MXFP8 output (codes + block scales; N a multiple of 32)
     if (c.swiglu_h <= 0 || !c.gather || c.scatter || !c.c_scales || c.N % 32 != 0) return hipErrorInvalidValue;
-    using S = ShapeLargeMX;
     const int64_t ntn = (c.N + S::BN / 2 - 1) / (S::BN / 2);
     const int64_t upper = static_cast<int64_t>(c.tiles.cap) * ntn;
     if (upper <= 0 || c.rows_bound <= 0) return hipSuccess;
@@ -848,7 +868,16 @@ hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s) {
                        dim3(S::NT), 0, s, c);
     return hipGetLastError();
   }
-  return launch_shape<ShapeLargeMX>(c, s, ShapeLargeMX::WG_PER_CU);
+  return launch_shape<S>(c, s, S::WG_PER_CU);
+}
+
+hipError_t launch_gemm_mx(const GemmCall& c, hipStream_t s) {
+  if (c.dense_M > 0 || c.Kd % ShapeLargeMX::BK != 0 || !c.a_scale || !c.b_scale) return hipErrorInvalidValue;
+  // four k-stages of scales per 16-byte load: whole groups, 16-byte aligned rows
+  const bool grouped = c.Kd % (4 * ShapeLargeMXG::BK) == 0 && c.a_scale_ld % 16 == 0 && c.b_scale_ld % 16 == 0 &&
+                       c.b_scale_group_stride % 16 == 0 && reinterpret_cast<uintptr_t>(c.a_scale) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(c.b_scale) % 16 == 0;
+  return grouped ? launch_mx_shape<ShapeLargeMXG>(c, s) : launch_mx_shape<ShapeLargeMX>(c, s);
 }
 
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s) {
