@@ -522,7 +522,13 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // the last staging round: its loads then overlap the last round's reads and stores. (Issued
   // earlier, the compiler would wait for them before the staging writes, which share LDS.)
   auto epilogue = [&](const TileState& t, bool more, int64_t it_next, TileState& nx) {
-    const int quad = 4 * (lane >> 5);
+    // The thread index passes through an empty asm statement: the epilogue's per-lane addresses
+    // are then computed here, not hoisted out of the persistent loop, where they would hold
+    // registers through every k-stage.
+    int etid = tid;
+    asm volatile("" : "+v"(etid));
+    const int elane = etid & 63;
+    const int quad = 4 * (elane >> 5);
     const int64_t col0 = t.nt * OUTC;
 #pragma unroll
     for (int rho = 0; rho < NR; ++rho) {
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       if constexpr (SCATTER) {
 #pragma unroll
         for (int k = 0; k < KI; ++k) {
-          const int m = tile_row(rho, k * RPI + tid / CPR);
+          const int m = tile_row(rho, k * RPI + etid / CPR);
           sidx[k] = c.scatter[min(t.row0 + (m < t.rows ? m : 0), c.rows_bound - 1)];
         }
       }
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
       for (int ii = 0; ii < TMR; ++ii) {
         const int i = rho * TMR + ii;
-        const int lr = wm * TMR * 32 + ii * 32 + (lane & 31);
+        const int lr = wm * TMR * 32 + ii * 32 + (elane & 31);
         if (SWIGLU) {
 #pragma unroll
           for (int j = 0; j < S::TN / 2; ++j) {
@@ -563,7 +569,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
               if constexpr (H_OUT) {
                 // training forward: the pre-activation H (bf16, [up | gate]) of this lane's
                 // 4 columns, stored straight from the registers
-                const int m = wm * S::TM * 32 + i * 32 + (lane & 31);
+                const int m = wm * S::TM * 32 + i * 32 + (elane & 31);
                 const int64_t hc = col0 + ct;
                 if (m < t.rows && hc < c.N) {
                   uint16_t* hr = static_cast<uint16_t*>(c.h_out) + min(t.row0 + m, c.rows_bound - 1) * 2 * c.swiglu_h;
@@ -613,18 +619,18 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       if constexpr (SCATTER) wait_vmcnt<0>();
       // The accumulators are dead once the last round is in LDS: set up the next tile then
       // (its index loads, then its first DMA loads, ahead of this round's stores).
-      const int cc = tid % CPR;
+      const int cc = etid % CPR;
       const int64_t col = col0 + cc * EPC;
       u32x4_t v[KI];
 #pragma unroll
-      for (int k = 0; k < KI; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg_addr(k * RPI + tid / CPR, cc * 16));
+      for (int k = 0; k < KI; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg_addr(k * RPI + etid / CPR, cc * 16));
       if (rho == NR - 1 && more) {
         setup(it_next, nx);
         if (!WGRAD || nx.nk > 0) issue(nx, 0, 0);
       }
 #pragma unroll
       for (int k = 0; k < KI; ++k) {
-        const int lr = k * RPI + tid / CPR;
+        const int lr = k * RPI + etid / CPR;
         const int m = tile_row(rho, lr);
         const int64_t orow = SCATTER ? static_cast<int64_t>(sidx[SCATTER ? k : 0]) : t.row0 + m;
         if constexpr (SWIGLU_BWD) {
