@@ -31,7 +31,9 @@
 //   * Epilogue through LDS: the accumulators leave the MFMA layout as 8-byte pieces of 32
 //     different rows, so stored directly every instruction writes 32 partial lines. They are
 //     staged in the free ring slot instead and stored as whole rows (full 128-byte lines per
-//     instruction); the next tile's first stage is issued during the last staging round.
+//     instruction). Large bf16 tiles issue the next tile's first stage as the epilogue starts
+//     (its list entry and row indices were fetched during the current tile), other shapes
+//     during the last staging round.
 //   * Experts with no tokens have no M-tile and their weights are never read.
 #include <type_traits>
 
@@ -134,6 +136,24 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// 8- and 16-byte LDS writes through inline asm, for the epilogue's staging: the compiler's
+// wait-count insertion does not count them as LDS accesses, so it does not hold them until
+// DMA loads in flight into the other ring slot have landed (it cannot always prove the two
+// LDS arrays apart). The epilogue waits for them itself (lgkmcnt) before the barrier that
+// publishes them; "memory" keeps them in order with the other memory operations.
+typedef uint32_t u32x2s __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_store_b64(void* p, uint32_t lo, uint32_t hi) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(p)));
+  const u32x2s d = {lo, hi};
+  asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(d) : "memory");
+}
+__device__ __forceinline__ void lds_store_b128(void* p, float x, float y, float z, float w) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(p)));
+  const u32x4s d = {__float_as_uint(x), __float_as_uint(y), __float_as_uint(z), __float_as_uint(w)};
+  asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(d) : "memory");
+}
+
 // Instruction-scheduling directives for one pipeline stage: step 0's LDS reads first, then in
 // each k16 step pair MFMAs with the next step's LDS reads and with this stage's share of the
 // global->LDS loads, so neither the LDS round trip nor the address unit stalls the matrix pipe.
@@ -208,6 +228,18 @@ __device__ __forceinline__ void sched_stage() {
   sched_stage_step<0, KSTEPS, KREADS, KMFMA, KLOADS, KLOADS>();
 }
 
+// MXFP8 scale groups (shapes with four k-stages of scales per load): their own LDS array;
+// other shapes have none.
+template <class S>
+__device__ __forceinline__ unsigned char* scale_area() {
+  if constexpr (S::SCHALF > 0) {
+    __shared__ __attribute__((aligned(1024))) unsigned char a[2 * S::SCHALF];
+    return a;
+  } else {
+    return nullptr;
+  }
+}
+
 // TRANS: bit 0 = the token operand A is contraction-major, bit 1 = the weight operand B is (see
 // GemmCall::trans). WGRAD: weight-gradient mode, the contraction runs over each group's rows
 // (GemmCall::group_offsets). SWIGLU_BWD: the SwiGLU-backward epilogue (GemmCall::bwd_h).
@@ -227,7 +259,12 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   static_assert(!SWIGLU || S::TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
   static_assert(!SWIGLU || S::PLANES == 1, "planes are for plain products");
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[S::LDS];
+  // The two ring slots (and the MXFP8 scale groups) are separate LDS arrays, so the compiler
+  // can tell that DMA loads into one slot never touch another: it then does not hold the
+  // epilogue's staging in slot 1 until the next tile's loads into slot 0 have landed.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[S::STAGE];
+  unsigned char* const ldssc = scale_area<S>();
   const int tid = threadIdx.x, lane = tid & 63;
   // wavefront coordinates are uniform per wavefront: keep them in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -272,9 +309,20 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // The load index inside a stage is uniform per wavefront, so is the operand it reads.
   auto load_is_a = [&](int q) { return wave + S::NW * q < S::BM / S::kRowsPerDma; };
 
+  // What a tile's setup reads from memory, fetched one tile ahead (during the previous tile's
+  // k-loop) so that the next tile's first loads can be issued as soon as its epilogue starts:
+  // the tile's coordinates, its list entry, and the source row of each of this lane's
+  // token-row loads (and, MXFP8, of its scale row).
+  struct TileFetch {
+    int64_t nt, row0, grp, kb;
+    int rows, kcnt;
+    int32_t src[S::NQ];  // token-row loads: source row of the A operand
+    int32_t scsrc;       // MXFP8 scale loads of token rows: source row
+  };
+
   // it: the tile's slot in this XCD's chunk, or (weight-gradient mode) its index in the
   // heavy-first sequence handed out by the tile counter
-  auto setup = [&](int64_t it, TileState& t) {
+  auto fetch = [&](int64_t it, TileFetch& f) {
     int64_t mt;
     if (WGRAD) {
       // groups in the given order (most rows first), each group's M-tiles x N-tiles in turn
@@ -284,7 +332,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
                                             static_cast<int64_t>(c.groups) - 1)
                                       : r;
       mt = g * wg_mtiles + local / ntn;
-      t.nt = local % ntn;
+      f.nt = local % ntn;
     } else {
       const int64_t lin = xcd * chunk + it;
       // tiles go in groups of kGroupM M-tiles x all N-tiles
@@ -293,34 +341,68 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       const int64_t gm = min(static_cast<int64_t>(kGroupM), total_m - first_m);
       const int64_t local = lin - grp_i * gsz;
       mt = first_m + local % gm;
-      t.nt = local / gm;
+      f.nt = local / gm;
     }
-    int64_t grp;
+    f.kcnt = 0;
+    f.kb = 0;
+    if (WGRAD) {
+      f.grp = mt / wg_mtiles;
+      f.row0 = (mt - f.grp * wg_mtiles) * S::BM;
+      f.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - f.row0));
+      const int64_t kb = min(max(static_cast<int64_t>(c.group_offsets[f.grp]), int64_t(0)), c.rows_bound);
+      const int64_t ke = min(max(static_cast<int64_t>(c.group_offsets[f.grp + 1]), kb), c.rows_bound);
+      f.kb = kb;
+      f.kcnt = static_cast<int>(ke - kb);
+    } else if (c.dense_M > 0) {
+      f.row0 = mt * S::BM;
+      f.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - f.row0));
+      f.grp = 0;
+    } else {
+      f.row0 = c.tiles.row0[mt];
+      f.rows = c.tiles.rows[mt];
+      f.grp = c.tiles.expert[mt];
+    }
+#pragma unroll
+    for (int q = 0; q < S::NQ; ++q) {
+      f.src[q] = 0;
+      const int i = wave + S::NW * q;
+      // (the first condition is known at compile time: loads past it read weight rows)
+      if (S::NW * q >= S::BM / S::kRowsPerDma || !load_is_a(q) || TA) continue;
+      const int r = i * S::kRowsPerDma + dma_row;
+      int64_t p = f.row0 + (r < f.rows ? r : 0);
+      p = min(max(p, int64_t(0)), c.rows_bound - 1);
+      f.src[q] = static_cast<int32_t>(GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p);
+    }
+    f.scsrc = 0;
+    if constexpr (S::MX) {
+      const int r = wave * 64 + lane;
+      if (wave < S::NSC && r < S::BM) {
+        int64_t p = f.row0 + (r < f.rows ? r : 0);
+        p = min(max(p, int64_t(0)), c.rows_bound - 1);
+        f.scsrc = static_cast<int32_t>(GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p);
+      }
+    }
+  };
+
+  // The tile's load offsets from what fetch() read (registers only).
+  auto setup_fetched = [&](const TileFetch& f, TileState& t) {
+    t.nt = f.nt;
+    t.row0 = f.row0;
+    t.rows = f.rows;
+    const int64_t grp = f.grp;
     t.nk = static_cast<int>(c.Kd / S::BK);
     t.kcnt = 0;
     t.cofs = 0;
     t.Abase = Ab;
     if (WGRAD) {
-      grp = mt / wg_mtiles;
-      t.row0 = (mt - grp * wg_mtiles) * S::BM;
-      t.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - t.row0));
-      const int64_t kb = min(max(static_cast<int64_t>(c.group_offsets[grp]), int64_t(0)), c.rows_bound);
-      const int64_t ke = min(max(static_cast<int64_t>(c.group_offsets[grp + 1]), kb), c.rows_bound);
-      t.kcnt = static_cast<int>(ke - kb);
+      t.kcnt = f.kcnt;
       t.nk = (t.kcnt + S::BK - 1) / S::BK;
       t.cofs = grp * c.c_group_stride;
-      t.Abase = Ab + kb * c.lda * 2;
-      t.Bexp = static_cast<const unsigned char*>(c.B) + kb * c.ldb * 2;
-    } else if (c.dense_M > 0) {
-      t.row0 = mt * S::BM;
-      t.rows = static_cast<int>(min(static_cast<int64_t>(S::BM), c.dense_M - t.row0));
-      grp = 0;
+      t.Abase = Ab + f.kb * c.lda * 2;
+      t.Bexp = static_cast<const unsigned char*>(c.B) + f.kb * c.ldb * 2;
     } else {
-      t.row0 = c.tiles.row0[mt];
-      t.rows = c.tiles.rows[mt];
-      grp = c.tiles.expert[mt];
+      t.Bexp = static_cast<const unsigned char*>(c.B) + grp * c.b_group_stride * S::EB;
     }
-    if (!WGRAD) t.Bexp = static_cast<const unsigned char*>(c.B) + grp * c.b_group_stride * S::EB;
 #pragma unroll
     for (int q = 0; q < S::NQ; ++q) {
       const int i = wave + S::NW * q;
@@ -341,10 +423,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // the logical chunk this lane fetches, so that the linear LDS write lands swizzled
       const int chunk_l = (lane % S::CHUNKS) ^ ((r / S::ROWS_PER_BANKLINE) & (S::CHUNKS - 1));
       if (is_a) {
-        int64_t p = t.row0 + (r < t.rows ? r : 0);
-        p = min(max(p, int64_t(0)), c.rows_bound - 1);
-        int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
-        src = min(max(src, int64_t(0)), c.a_rows - 1);
+        const int64_t src = min(max(static_cast<int64_t>(f.src[q]), int64_t(0)), c.a_rows - 1);
         t.src_off[q] = static_cast<uint32_t>(src * c.lda * S::EB + chunk_l * 16);
       } else {
         int64_t wrow;
@@ -369,10 +448,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       if (wave < S::NSC) {
         const int r = wave * 64 + lane;
         if (r < S::BM) {
-          int64_t p = t.row0 + (r < t.rows ? r : 0);
-          p = min(max(p, int64_t(0)), c.rows_bound - 1);
-          int64_t src = GATHER ? static_cast<int64_t>(c.gather[p]) / c.gather_div : p;
-          src = min(max(src, int64_t(0)), c.a_rows - 1);
+          const int64_t src = min(max(static_cast<int64_t>(f.scsrc), int64_t(0)), c.a_rows - 1);
           t.sc_base = c.a_scale;
           t.sc_off = static_cast<uint32_t>(src * c.a_scale_ld);
         } else {
@@ -394,9 +470,14 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     }
   };
 
-  // DMA loads of k-stage kt of tile t into ring slot `ring_slot`.
-  auto issue = [&](const TileState& t, int kt, int ring_slot) {
-    unsigned char* st = lds + ring_slot * S::STAGE;
+  auto setup = [&](int64_t it, TileState& t) {
+    TileFetch f;
+    fetch(it, f);
+    setup_fetched(f, t);
+  };
+
+  // DMA loads of k-stage kt of tile t into ring slot `st` (lds0 or lds1).
+  auto issue = [&](const TileState& t, int kt, unsigned char* st) {
 #pragma unroll
     for (int q = 0; q < S::NQ; ++q) {
       const int i = wave + S::NW * q;
@@ -425,7 +506,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // kt / 4 - 2 used, whose last reader (stage kt - 5) every wavefront has passed.
       if (wave < S::NSC && (kt & 3) == 0)
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(t.sc_base + (t.sc_off + static_cast<uint32_t>(kt) * 4)),
-                                         LDS_PTR(lds + S::NSTAGE * S::STAGE + ((kt >> 2) & 1) * S::SCHALF + wave * 1024),
+                                         LDS_PTR(ldssc + ((kt >> 2) & 1) * S::SCHALF + wave * 1024),
                                          16, 0, 0);
     }
   };
@@ -506,7 +587,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   constexpr int RPI = S::NT * 16 / RB;                  // rows per store instruction
   constexpr int KI = RR / RPI;                          // store instructions per thread per round
   static_assert(S::TM % NR == 0 && RR % RPI == 0 && RR * RB <= S::STAGE, "epilogue staging");
-  unsigned char* stg = lds + S::STAGE;
+  unsigned char* stg = lds1;
   // LDS byte address of byte b of staged row lr: 16-byte chunks XOR-swizzled by row, so the
   // 32 rows of one register group land in distinct bank groups and a row read stays whole.
   auto stg_addr = [&](int lr, int b) {
@@ -521,7 +602,14 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // Epilogue of tile t. When `more`, stage 0 of tile nx is issued into slot 0 once slot 1 holds
   // the last staging round: its loads then overlap the last round's reads and stores. (Issued
   // earlier, the compiler would wait for them before the staging writes, which share LDS.)
-  auto epilogue = [&](const TileState& t, bool more, int64_t it_next, TileState& nx) {
+  // Large tiles issue the next tile's first stage as soon as the epilogue starts (its list
+  // entry and row indices were fetched during this tile's k-loop), so those loads overlap the
+  // whole epilogue; they fill ring slot 0 while the epilogue stages through slot 1. There every
+  // wavefront issues exactly NQ operand loads (plus one scale load for MXFP8 wavefronts below
+  // NSC), the count the scatter wait below relies on. Other shapes issue it in the last round.
+  constexpr bool EARLY = !WGRAD && !S::MX && S::BM == 256 && S::NI % S::NW == 0;
+  constexpr int NSIDX = SCATTER ? (EARLY ? NR * KI : KI) : 1;
+  auto epilogue = [&](const TileState& t, bool more, const TileFetch& fn, int64_t it_next, TileState& nx) {
     // The thread index passes through an empty asm statement: the epilogue's per-lane addresses
     // are then computed here, not hoisted out of the persistent loop, where they would hold
     // registers through every k-stage.
@@ -530,18 +618,34 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int elane = etid & 63;
     const int quad = 4 * (elane >> 5);
     const int64_t col0 = t.nt * OUTC;
+    // Scatter indices of the rows this thread stores in round rho (all rounds up front when the
+    // next tile's loads follow them), fetched first so their latency overlaps the LDS round trip.
+    int sidx[NSIDX];
+    auto load_sidx = [&](int rho, int base) {
+#pragma unroll
+      for (int k = 0; k < KI; ++k) {
+        const int m = tile_row(rho, k * RPI + etid / CPR);
+        sidx[base + k] = c.scatter[min(t.row0 + (m < t.rows ? m : 0), c.rows_bound - 1)];
+      }
+    };
+    if constexpr (SCATTER && EARLY) {
+#pragma unroll
+      for (int rho = 0; rho < NR; ++rho) load_sidx(rho, rho * KI);
+    }
+    if constexpr (EARLY) {
+      // The same loads are in flight after the indices on every path: with no next tile the
+      // current tile's first stage is loaded again (valid addresses, into the free slot 0,
+      // never read; the exit waits for it).
+      if (more) {
+        setup_fetched(fn, nx);
+        issue(nx, 0, lds0);
+      } else {
+        issue(t, 0, lds0);
+      }
+    }
 #pragma unroll
     for (int rho = 0; rho < NR; ++rho) {
-      // Scatter indices of the rows this thread stores in this round, fetched first so their
-      // latency overlaps the LDS round trip.
-      int sidx[SCATTER ? KI : 1];
-      if constexpr (SCATTER) {
-#pragma unroll
-        for (int k = 0; k < KI; ++k) {
-          const int m = tile_row(rho, k * RPI + etid / CPR);
-          sidx[k] = c.scatter[min(t.row0 + (m < t.rows ? m : 0), c.rows_bound - 1)];
-        }
-      }
+      if constexpr (SCATTER && !EARLY) load_sidx(rho, 0);
       if (rho > 0) {  // every wavefront done reading the previous round
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
@@ -585,9 +689,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
                   *reinterpret_cast<uint2*>(hr + c.swiglu_h + hc) = make_uint2(gv[0], gv[1]);
                 }
               }
-              *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
-                  make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                             o[2] | (static_cast<uint32_t>(o[3]) << 16));
+              lds_store_b64(stg + stg_addr(lr, ct * 2), o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                            o[2] | (static_cast<uint32_t>(o[3]) << 16));
             }
           }
         } else {
@@ -597,15 +700,14 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int g = 0; g < 4; ++g) {
               const int ct = wn * (S::TN * 32) + j * 32 + 8 * g + quad;
               if constexpr (OUT_F32) {
-                *reinterpret_cast<float4*>(stg + stg_addr(lr, ct * 4)) =
-                    make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                lds_store_b128(stg + stg_addr(lr, ct * 4), acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                               acc[i][j][4 * g + 3]);
               } else {
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16_bits(acc[i][j][4 * g + r]);
-                *reinterpret_cast<uint2*>(stg + stg_addr(lr, ct * 2)) =
-                    make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                               o[2] | (static_cast<uint32_t>(o[3]) << 16));
+                lds_store_b64(stg + stg_addr(lr, ct * 2), o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                              o[2] | (static_cast<uint32_t>(o[3]) << 16));
               }
             }
           }
@@ -616,23 +718,41 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       // The scatter indices of this round (loaded at its start) are waited for once here; left
       // to the compiler, every store would wait for all vector-memory operations in flight
       // (the next tile's first loads and the previous stores) before using its index.
-      if constexpr (SCATTER) wait_vmcnt<0>();
-      // The accumulators are dead once the last round is in LDS: set up the next tile then
-      // (its index loads, then its first DMA loads, ahead of this round's stores).
+      // (EARLY: only the next tile's loads were issued after the indices, and loads complete
+      // in order, so waiting until that many remain in flight is enough.)
+      if constexpr (SCATTER) {
+        if constexpr (EARLY) {
+          if (rho == 0) {
+            // Once they have landed the indices pass through an empty asm statement: they are
+            // then no longer load results to the compiler, which would otherwise wait for every
+            // load in flight (the next tile's too) before each store.
+            static_assert(!EARLY || !S::MX, "the wait below counts operand loads only");
+            wait_vmcnt<S::NQ>();
+#pragma unroll
+            for (int k = 0; k < NSIDX; ++k) asm volatile("" : "+v"(sidx[k]));
+          }
+        } else {
+          wait_vmcnt<0>();
+        }
+      }
       const int cc = etid % CPR;
       const int64_t col = col0 + cc * EPC;
       u32x4_t v[KI];
 #pragma unroll
       for (int k = 0; k < KI; ++k) v[k] = *reinterpret_cast<const u32x4_t*>(stg + stg_addr(k * RPI + etid / CPR, cc * 16));
-      if (rho == NR - 1 && more) {
-        setup(it_next, nx);
-        if (!WGRAD || nx.nk > 0) issue(nx, 0, 0);
+      // Other shapes: the accumulators are dead once the last round is in LDS; set up the next
+      // tile then (its index loads, then its first DMA loads, ahead of this round's stores).
+      if constexpr (!EARLY) {
+        if (rho == NR - 1 && more) {
+          setup(it_next, nx);
+          if (!WGRAD || nx.nk > 0) issue(nx, 0, lds0);
+        }
       }
 #pragma unroll
       for (int k = 0; k < KI; ++k) {
         const int lr = k * RPI + etid / CPR;
         const int m = tile_row(rho, lr);
-        const int64_t orow = SCATTER ? static_cast<int64_t>(sidx[SCATTER ? k : 0]) : t.row0 + m;
+        const int64_t orow = SCATTER ? static_cast<int64_t>(sidx[SCATTER ? (EARLY ? rho * KI : 0) + k : 0]) : t.row0 + m;
         if constexpr (SWIGLU_BWD) {
           // v holds 8 columns of d_act (bf16) of sorted row orow; with the saved up / gate of
           // those columns: d_up = d_act * silu(gate), d_gate = d_act * up * silu'(gate),
@@ -716,9 +836,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   int64_t it = WGRAD ? static_cast<int64_t>(sched[0]) : blockIdx.x / kXcds;
   if (WGRAD ? it >= total : (it >= chunk || xcd * chunk + it >= total)) return;
   int parity = 1;
+  TileFetch fnext;
   TileState cur;
   setup(it, cur);
-  if (!WGRAD || cur.nk > 0) issue(cur, 0, 0);
+  if (!WGRAD || cur.nk > 0) issue(cur, 0, lds0);
   for (;;) {
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
@@ -729,14 +850,20 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 
     if (WGRAD && tid == 0) sched[parity] = atomicAdd(c.tile_counter, 1);
     const int nk = WGRAD ? cur.nk : static_cast<int>(c.Kd / S::BK);
-    for (int kt = 0; kt < nk; ++kt) {
+    // EARLY: the next tile of this workgroup's sequence, fetched during the first stage
+    const int64_t it_pre = it + per_xcd;
+    const bool fetch_next = EARLY && it_pre < chunk && xcd * chunk + it_pre < total;
+    if (fetch_next && nk <= 0) fetch(it_pre, fnext);
+    // Stage kt reads slot `la` (lds0 for even kt, lds1 for odd) and refills the other one; the
+    // loop runs two stages per iteration so that each stage's slot is known at compile time.
+    auto kstage = [&](int kt, const unsigned char* la, unsigned char* other) {
       // This wavefront's loads of stage kt have landed; after the barrier so have every
       // wavefront's, and every wavefront is done reading stage kt-1, whose slot is refilled.
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      const unsigned char* la = lds + (kt & 1) * S::STAGE;
       const unsigned char* lb = la + S::BM * S::ROWB;
-      if (kt + 1 < nk) issue(cur, kt + 1, (kt + 1) & 1);
+      if (kt + 1 < nk) issue(cur, kt + 1, other);
+      if (fetch_next && kt == 0) fetch(it_pre, fnext);
       // k16 steps with fragments double-buffered in registers; the directives interleave step
       // kk+1's LDS reads with step kk's MFMAs so the matrix pipe does not wait on an LDS round
       // trip before every MFMA group.
@@ -745,7 +872,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         if constexpr (S::SCG == 1)
           lds_scales(la + S::DATA, 4);
         else
-          lds_scales(lds + S::NSTAGE * S::STAGE + ((kt >> 2) & 1) * S::SCHALF + (kt & 3) * 4, 16);
+          lds_scales(ldssc + ((kt >> 2) & 1) * S::SCHALF + (kt & 3) * 4, 16);
         lds_frags_mx(0, la, lb, 0);
 #pragma unroll
         for (int kk = 0; kk < S::BK / 64; ++kk) {
@@ -775,6 +902,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         }
         sched_stage<kSteps, kReads, kMfma, 0>();
       }
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      kstage(kt, lds0, lds1);
+      if (kt + 1 < nk) kstage(kt + 1, lds1, lds0);
     }
     // Every wavefront done reading this tile's last stages: slot 0 is free for the next tile.
     // (Weight-gradient mode: a full workgroup barrier with fences, which also publishes the
@@ -797,7 +928,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       more = it_next < chunk && xcd * chunk + it_next < total;
     }
     TileState nxt;
-    epilogue(cur, more, it_next, nxt);
+    epilogue(cur, more, fnext, it_next, nxt);
     if (!more) break;
     cur = nxt;
     it = it_next;
