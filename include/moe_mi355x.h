@@ -151,7 +151,9 @@ typedef struct moe_routing_t {
                                       capacity, of the kept counts min(count, capacity)        */
   int32_t* permutation;            /* (A) int32: sorted position p -> assignment t*k+j; with a
                                       capacity, positions >= expert_offsets[E] hold the dropped
-                                      assignments (same stable order)                          */
+                                      assignments (same stable order); positions past the
+                                      placed assignments (only when moe_permute is given
+                                      entries the routing never produces) hold -1             */
   int32_t* inverse_permutation;    /* (A) int32: assignment t*k+j -> sorted position p          */
   float* router_logits;            /* (T, E) fp32 logits                                       */
   float* router_scores;            /* (T, E) fp32 gating scores (softmax or sigmoid+eps)       */
@@ -239,8 +241,9 @@ MOE_API moe_status_t moe_route_from_scores(const moe_config_t* cfg, int64_t num_
  * Token counts and the stable permutation: [OC3 "Пересылка токенов между экспертами"] (sort
  * the expert indices; bins = cumsum of counts) and [OC3 "Балансировка нагрузки и
  * вспомогательные штрафы"] (per-expert histogram). expert_indices (T, k) int32 in [0, E),
- * distinct within a row (not checked on the device; out-of-range entries are not counted and
- * get no position). Outputs (all required): batch_size_per_expert (E), expert_offsets (E+1),
+ * distinct within a row (the routing always gives such rows; an entry out of [0, E), or one
+ * that repeats an earlier expert of its row, is not counted and gets no position: its inverse
+ * is -1 and it occupies no slot below expert_offsets[E]). Outputs (all required): batch_size_per_expert (E), expert_offsets (E+1),
  * permutation (A), inverse_permutation (A); the permutation is the stable sort of t*k+j by
  * expert. With cfg.capacity_factor > 0 ([OC3 "Ёмкость эксперта и переполнение"]) each expert
  * keeps the first `capacity` assignments of that order: the offsets delimit the kept rows, the

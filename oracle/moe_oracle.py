@@ -143,15 +143,21 @@ def _f64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
+def _acc(a, acc) -> np.ndarray:
+    """The operand of a contraction in the accumulation dtype: float64 (the default, for
+    checking) or float32 (the mode the CPU timing uses; the products then sum in fp32 BLAS)."""
+    return np.asarray(a, dtype=acc)
+
+
 # ----------------------------------------------------------------------------- router
 
-def router_logits(x, router_weight, router_bias=None) -> np.ndarray:
+def router_logits(x, router_weight, router_bias=None, acc=np.float64) -> np.ndarray:
     """[OC3 "Маршрутизация"]: the router input is cast to fp32 and a linear layer with an
     (num_experts, d_model) weight gives the (tokens, num_experts) logits. [OC3 "Как задаётся
     конфигурация MoE"]: the router has d_model*num_experts weights plus num_experts bias terms
     when bias is on. The dot products are summed in float64 and rounded to fp32 once.
     Eval mode: the training-only jitter of [OC3 "Jitter при обучении"] is a no-op."""
-    l = _f64(x) @ _f64(router_weight).T
+    l = _acc(x, acc) @ _acc(router_weight, acc).T
     if router_bias is not None:
         l = l + _f64(router_bias)[None, :]
     return round_f32(l)
@@ -418,16 +424,16 @@ def expert_mlp_mxfp8(cfg: "MoEConfig", z_rows, w1_e, w2_e) -> np.ndarray:
 
 # ---------------------------------------------------------------------- experts
 
-def prepare_routed_input(cfg: MoEConfig, x, down_proj=None) -> np.ndarray:
+def prepare_routed_input(cfg: MoEConfig, x, down_proj=None, acc=np.float64) -> np.ndarray:
     """[OC3 "Латентная проекция экспертов"]: without a latent projection the experts get the
     input unchanged; with one, a down-projection maps (*, d_model) to (*, latent_dim). The
     result is stored in the layer dtype."""
     if not cfg.latent_dim:
         return _f64(x)
-    return round_to(_f64(x) @ _f64(down_proj).T, cfg.dtype)
+    return round_to(_acc(x, acc) @ _acc(down_proj, acc).T, cfg.dtype)
 
 
-def expert_mlp(cfg: MoEConfig, z_rows, w1_e, w2_e) -> np.ndarray:
+def expert_mlp(cfg: MoEConfig, z_rows, w1_e, w2_e, acc=np.float64) -> np.ndarray:
     """One expert's SwiGLU MLP on its rows.
 
     [OC3 "Как задаётся конфигурация MoE"]: up_factor is 2 for swiglu, so the first matrix
@@ -437,14 +443,14 @@ def expert_mlp(cfg: MoEConfig, z_rows, w1_e, w2_e) -> np.ndarray:
     экспертов и точность"]: the grouped experts return bf16 (fp32 for an fp32 layer).
     Weights are (2h, K) and (K, h), out x in."""
     h = cfg.hidden_size
-    H = _f64(z_rows) @ _f64(w1_e).T
+    H = _acc(z_rows, acc) @ _acc(w1_e, acc).T
     up, gate = H[:, :h], H[:, h:]
     with np.errstate(over="ignore"):
         act = round_to(up * gate / (1.0 + np.exp(-gate)), cfg.dtype)
-    return round_to(act @ _f64(w2_e).T, cfg.dtype)
+    return round_to(_acc(act, acc) @ _acc(w2_e, acc).T, cfg.dtype)
 
 
-def run_experts(cfg: MoEConfig, z, idx, w1, w2, capacity: Optional[int] = None) -> dict:
+def run_experts(cfg: MoEConfig, z, idx, w1, w2, capacity: Optional[int] = None, acc=np.float64) -> dict:
     """[OC3 "Вычисления экспертов и точность"]: group the permuted tokens by expert, run each
     expert's MLP, and return the results; Y is kept in sorted (permuted) order here.
     w1/w2 may be arrays (E, ...) or mappings expert -> array (only touched experts needed).
@@ -456,12 +462,14 @@ def run_experts(cfg: MoEConfig, z, idx, w1, w2, capacity: Optional[int] = None) 
     kept_counts = counts if capacity is None else np.minimum(counts, capacity)
     offsets = expert_offsets(kept_counts)
     perm, inv, kept = capacity_permutation(idx, cfg.num_experts, capacity)
-    z_perm = _f64(z)[perm // k]
-    Y = np.zeros((perm.size, _f64(z).shape[1]))
-    mlp = expert_mlp_mxfp8 if cfg.expert_precision == "mxfp8" else expert_mlp
+    z_perm = _acc(z, acc)[perm // k]
+    Y = np.zeros((perm.size, z_perm.shape[1]), dtype=acc)  # holds layer-dtype values: exact in fp32 too
     for e in np.nonzero(kept_counts)[0]:
         rows = slice(offsets[e], offsets[e + 1])
-        Y[rows] = mlp(cfg, z_perm[rows], w1[e], w2[e])
+        if cfg.expert_precision == "mxfp8":
+            Y[rows] = expert_mlp_mxfp8(cfg, z_perm[rows], w1[e], w2[e])
+        else:
+            Y[rows] = expert_mlp(cfg, z_perm[rows], w1[e], w2[e], acc)
     return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, kept=kept, z_perm=z_perm, Y=Y)
 
 
@@ -498,18 +506,20 @@ def restore_routed_output(cfg: MoEConfig, o, norm_weight=None, up_proj=None) -> 
     return dict(n=n, y=n @ _f64(up_proj).T)
 
 
-def forward(cfg: MoEConfig, weights: dict, x) -> dict:
+def forward(cfg: MoEConfig, weights: dict, x, acc=np.float64) -> dict:
     """The whole layer, step by step. `weights` holds numpy arrays (bf16 values as float32):
     router_weight (E,d), router_bias (E)|None, score_bias (E)|None, down_proj (L,d)|None,
     norm_weight (L)|None, up_proj (d,L)|None, w1 (E,2h,K) or {e: (2h,K)}, w2 (E,K,h) or
-    {e: (K,h)}. The final y is returned unrounded (float64)."""
+    {e: (K,h)}. The final y is returned unrounded (float64). acc = np.float32 sums the
+    contractions (router, latent down, expert matmuls) in fp32 instead of float64: the mode
+    the CPU timing runs in; every rounding point stays where it is."""
     out = {}
-    logits = router_logits(x, weights["router_weight"], weights.get("router_bias"))
+    logits = router_logits(x, weights["router_weight"], weights.get("router_bias"), acc)
     out.update(route(cfg, logits, weights.get("score_bias")))
-    z = prepare_routed_input(cfg, x, weights.get("down_proj"))
+    z = prepare_routed_input(cfg, x, weights.get("down_proj"), acc)
     out["z"] = z
     out["capacity"] = expert_capacity(cfg, np.asarray(x).shape[0])
-    out.update(run_experts(cfg, z, out["idx"], weights["w1"], weights["w2"], out["capacity"]))
+    out.update(run_experts(cfg, z, out["idx"], weights["w1"], weights["w2"], out["capacity"], acc))
     o = combine(cfg, out["Y"], out["inv"], out["w"])
     out["o"] = o
     out.update(restore_routed_output(cfg, o, weights.get("norm_weight"), weights.get("up_proj")))

@@ -45,8 +45,8 @@ def test_mx_quantize_bitexact(rows, cols, std):
     assert np.array_equal(codes.cpu().numpy(), want_c)
 
 
-from parity import (assert_close, bf16_spacing, check_routing_invariants, mx_expert_allowance, np32,  # noqa: E402
-                    oracle_inputs, routing_matches, to_device_weights)
+from parity import (assert_close, bf16_spacing, check_forward_routing, check_routing_invariants,  # noqa: E402
+                    mx_expert_allowance, np32, oracle_from_gpu_routing, oracle_inputs, to_device_weights)
 import workloads  # noqa: E402
 
 
@@ -105,15 +105,15 @@ def test_layer_mxfp8(case):
     y, r = layer(x.cuda(), routing=True)
     torch.cuda.synchronize()
     check_routing_invariants(cfg, r, T)
-    ref = O.forward(cfgO, oracle_inputs(w), np32(x))
-    key_tol = 1e-4 * max(1.0, float(np.abs(ref["keys"]).max()))
-    same = routing_matches(cfgO, r["expert_indices"].cpu().numpy(), ref, key_tol)
-    assert same.mean() >= 0.99
-    mx_error_report(np32(y)[same], ref["y"][same], f"layer {name}")
+    check_forward_routing(cfgO, r, w["score_bias"])
+    wo = oracle_inputs(w)
+    gi, gw = r["expert_indices"].cpu().numpy(), r["expert_weights"].cpu().numpy()
+    ref = oracle_from_gpu_routing(cfgO, wo, np32(x), gi, gw)
+    mx_error_report(np32(y), ref["y"], f"layer {name}")
     allow = None
     if not cfgO.latent_dim:
         # through the combine: sum_j |w_j| (allowance of Y_j + one bf16 spacing of Y_j)
-        a = mx_expert_allowance(cfgO, ref, oracle_inputs(w)) + bf16_spacing(ref["Y"])
-        allow = (np.abs(ref["w"])[:, :, None] * a[np.asarray(ref["inv"]).reshape(T, -1)]).sum(axis=1)[same]
-    assert_close(np32(y)[same], ref["y"][same], "bf16", f"layer mxfp8 {name}", allow,
+        a = mx_expert_allowance(cfgO, ref, wo) + bf16_spacing(ref["Y"])
+        allow = (np.abs(ref["w"])[:, :, None] * a[np.asarray(ref["inv"]).reshape(T, -1)]).sum(axis=1)
+    assert_close(np32(y), ref["y"], "bf16", f"layer mxfp8 {name}", allow,
                  budget_share=None if allow is None else 1.0)

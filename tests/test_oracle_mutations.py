@@ -11,7 +11,7 @@ import test_oracle_pins as P
 from oracle import moe_oracle as O
 
 
-def _swapped_up_gate(cfg, z_rows, w1_e, w2_e):
+def _swapped_up_gate(cfg, z_rows, w1_e, w2_e, acc=np.float64):
     h = cfg.hidden_size
     H = np.asarray(z_rows, np.float64) @ np.asarray(w1_e, np.float64).T
     gate, up = H[:, :h], H[:, h:]  # halves swapped

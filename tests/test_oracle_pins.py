@@ -620,3 +620,34 @@ def test_mxfp8_dense_bruteforce_equals_permuted_path():
     # and the MXFP8 layer stays close to the bf16 one (quantisation error only)
     ref = O.forward(dataclasses.replace(cfg, expert_precision="bf16"), w, x)
     assert np.linalg.norm(out["y"] - ref["y"]) <= 0.1 * np.linalg.norm(ref["y"])
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny_f32", {}),
+    ("olmoe", dict(tokens=300, d_model=256, num_experts=8, top_k=2, hidden_size=128)),
+    ("latent896", dict(tokens=200, d_model=256, latent_dim=128, num_experts=16, top_k=4, hidden_size=64)),
+])
+def test_float32_accumulation_mode_agrees_with_float64(name, over):
+    """The mode the CPU timing runs in (acc=float32) changes only the summation dtype of the
+    contractions, so it computes the same layer: equal routing except at near-ties, values
+    within the layer tolerance of the float64 oracle (fp32 layer: relative 1e-5; bf16 layers:
+    max-abs 2e-2 and relative Frobenius 1e-2)."""
+    over = dict(over)
+    T = over.pop("tokens", None)
+    cfg, w, x = workloads.make_workload(name, tokens=T, **over)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    wo = {k: workloads.to_numpy_f32(v) for k, v in w.items()}
+    xs = workloads.to_numpy_f32(x)
+    r64 = O.forward(cfgO, wo, xs)
+    r32 = O.forward(cfgO, wo, xs, acc=np.float32)
+    same = np.all(r64["idx"] == r32["idx"], axis=1)
+    assert same.mean() >= 0.99
+    d = np.abs(r32["y"][same] - r64["y"][same])
+    fro = np.linalg.norm(r32["y"][same] - r64["y"][same]) / np.linalg.norm(r64["y"][same])
+    if cfg["dtype"] == "f32":
+        assert fro <= 1e-5 and d.max() <= 1e-5 * np.abs(r64["y"]).max()
+    else:
+        assert fro <= 1e-2 and d.max() <= 2e-2
+    # the mode really sums in fp32: the logits differ from the float64 sums somewhere
+    l32 = O.router_logits(xs, wo["router_weight"], wo["router_bias"], acc=np.float32)
+    assert not np.array_equal(l32, r64["logits"])

@@ -723,22 +723,25 @@ moe_status_t moe_workspace_size(const moe_config_t* c, int64_t T, size_t* bytes)
   return ok();
 }
 
-moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* y,
-                         moe_routing_t* routing, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a whole-layer call (before any HIP call).
+moe_status_t check_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* y) {
   moe_status_t st = validate_config(c);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(c, T)) != MOE_OK) return st;
   if ((st = check_weights(c, w, true, true, true)) != MOE_OK) return st;
-  if (T == 0) return ok();
+  if (T == 0) return MOE_OK;
   if ((st = need(x, "x")) != MOE_OK) return st;
-  if ((st = need(y, "y")) != MOE_OK) return st;
-  if ((st = need(ws, "workspace")) != MOE_OK) return st;
-  const Layer ly = make_layer(c, T);
-  const WsLayout L = ws_layout(ly);
-  if (ws_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
-                                                 std::to_string(L.total));
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return need(y, "y");
+}
+
+// The launch sequence of the whole layer on a workspace of at least ws_layout(ly).total bytes.
+moe_status_t enqueue_forward(const Layer& ly, const WsLayout& L, const moe_weights_t* w, const void* x, void* y,
+                             moe_routing_t* routing, void* ws, hipStream_t s) {
+  const int64_t T = ly.T;
   moe_routing_t r{};
   if (routing) r = *routing;
   float* parts = at<float>(ws, L.logits);
@@ -780,6 +783,24 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
     MOE_TRY_HIP(launch_combine(ly, at<void>(ws, L.yassign), wts, nullptr, false, y, s), "combine");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* y,
+                         moe_routing_t* routing, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_forward(c, w, T, x, y);
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  if ((st = need(ws, "workspace")) != MOE_OK) return st;
+  const Layer ly = make_layer(c, T);
+  const WsLayout L = ws_layout(ly);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
+                                                 std::to_string(L.total));
+  return enqueue_forward(ly, L, w, x, y, routing, ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_router_forward(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x,

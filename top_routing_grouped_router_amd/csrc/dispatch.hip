@@ -24,6 +24,10 @@
 //   permute         one thread per copy: position = offset + block base + rank.
 //   dispatch_small  all of the above in one workgroup for batches of at most 1024 tokens,
 //                   where four launches would cost more than the work.
+// Entries that the routing never produces are handled alike by both paths: an index out of
+// [0, E), or one that repeats an earlier index of its token, is not counted and gets no
+// position (inverse -1). A repeat is seen in the mask ORs: the thread that owns the token ORs
+// its bit once per entry, in entry order, so a repeated expert finds its bit already set.
 // Everything here moves O(T*k) int32 words: a few MB at the largest shapes.
 #include <algorithm>
 
@@ -45,11 +49,15 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
   for (int e = lane; e < E; e += kWave) bits[wave * E + e] = 0;
   __syncthreads();
   const int64_t t = static_cast<int64_t>(b) * kRankTokens + wave * kWave + lane;
+  uint32_t rep = 0;  // bit j: entry j repeats an earlier expert of the token (k <= 16)
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]),
-                                    1ull << lane);
+      if (e >= 0 && e < E) {
+        const unsigned long long old = atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]),
+                                                1ull << lane);
+        if (old & (1ull << lane)) rep |= 1u << j;
+      }
     }
   }
   __syncthreads();
@@ -68,7 +76,7 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
       if (e >= 0 && e < E)
-        rank[t * k + j] = pre[wave * E + e] + __popcll(bits[wave * E + e] & below);
+        rank[t * k + j] = ((rep >> j) & 1u) ? -1 : pre[wave * E + e] + __popcll(bits[wave * E + e] & below);
     }
   }
 }
@@ -152,13 +160,16 @@ __device__ __forceinline__ void write_expert_tiles(int e, int excl, int c, const
 
 // counts -> offsets (or offsets given) -> M-tile lists. One block of 1024 threads, E <= 1024.
 // With a capacity (> 0) the offsets are those of the kept counts min(count, capacity), and
-// drop_off (E + 1) receives the exclusive scan of the dropped counts.
+// drop_off (E + 1) receives the exclusive scan of the dropped counts. With perm, the positions
+// past the kept and dropped assignments (those of entries that get no position) are set to -1
+// before permute_kernel writes the others.
 __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __restrict__ counts_in,
                                                              const int32_t* __restrict__ offsets_in,
                                                              int32_t* __restrict__ offsets_out,
                                                              int E, TilePlan plan, TileList tiles,
                                                              TileList small_tiles, int capacity,
-                                                             int32_t* __restrict__ drop_off) {
+                                                             int32_t* __restrict__ drop_off,
+                                                             int32_t* __restrict__ perm, int64_t A) {
   __shared__ int sh[17];
   const int e = threadIdx.x;
   int c = 0, excl = 0;
@@ -174,13 +185,19 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
     if (e < E) offsets_out[e] = excl;
     if (e == E - 1) offsets_out[E] = excl + c;
     __syncthreads();
+    int64_t placed = sh[16];  // kept assignments
+    __syncthreads();
     if (capacity > 0) {
       const int dc = n - c;
       const int dexcl = block_inclusive_scan(dc, sh) - dc;
       if (e < E) drop_off[e] = dexcl;
       if (e == E - 1) drop_off[E] = dexcl + dc;
       __syncthreads();
+      placed += sh[16];      // + dropped assignments
+      __syncthreads();
     }
+    if (perm)
+      for (int64_t p = placed + threadIdx.x; p < A; p += blockDim.x) perm[p] = -1;
   }
   if (tiles.cap <= 0) return;
   c = c < 0 ? 0 : c;
@@ -219,7 +236,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (a >= A) return;
   const int e = idx[a];
-  if (e < 0 || e >= E) {
+  if (e < 0 || e >= E || rank[a] < 0) {  // out of range, or a repeat within the token
     inv[a] = -1;
     return;
   }
@@ -301,7 +318,11 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   __syncthreads();
   for (int64_t a = tid; a < A; a += 256) {
     const int e = idx[a];
-    if (e >= 0 && e < E) atomicAdd(&run[e], 1);
+    if (e < 0 || e >= E) continue;
+    const int64_t row = a - a % k;
+    bool repeat = false;
+    for (int64_t q = row; q < a; ++q) repeat |= idx[q] == e;
+    if (!repeat) atomicAdd(&run[e], 1);
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
@@ -313,6 +334,8 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   __syncthreads();
   block_exclusive_scan_e(dc, E, doff, sh);
   __syncthreads();
+  // positions past the kept and dropped assignments belong to no entry
+  for (int64_t p = static_cast<int64_t>(off[E]) + doff[E] + tid; p < A; p += 256) perm[p] = -1;
   for (int e = tid; e < E; e += 256) {
     counts[e] = run[e];
     offsets[e] = off[e];
@@ -344,10 +367,15 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     for (int i = tid; i < 4 * E; i += 256) bits[i] = 0;
     __syncthreads();
     const int64_t t = t0 + tid;
+    uint32_t rep = 0;  // bit j: entry j repeats an earlier expert of the token
     if (t < T) {
       for (int j = 0; j < k; ++j) {
         const int e = idx[t * k + j];
-        if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]), 1ull << lane);
+        if (e >= 0 && e < E) {
+          const unsigned long long old =
+              atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]), 1ull << lane);
+          if (old & (1ull << lane)) rep |= 1u << j;
+        }
       }
     }
     __syncthreads();
@@ -365,7 +393,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
       for (int j = 0; j < k; ++j) {
         const int64_t a = t * k + j;
         const int e = idx[a];
-        if (e < 0 || e >= E) {
+        if (e < 0 || e >= E || ((rep >> j) & 1u)) {
           inv[a] = -1;
           continue;
         }
@@ -412,7 +440,7 @@ hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts,
                      blk);
   hipLaunchKernelGGL(scan_cols_kernel, dim3(ly.E), dim3(256), 0, s, blk, nblk, counts);
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, counts, nullptr, offsets, ly.E,
-                     plan, tiles, small_tiles, cap, drop_off);
+                     plan, tiles, small_tiles, cap, drop_off, perm, A);
   hipLaunchKernelGGL(permute_kernel, dim3(static_cast<unsigned>((A + 255) / 256)), dim3(256), 0, s,
                      idx, rank, blk, nblk, offsets, A, ly.k, ly.E, perm, inv, cap, drop_off);
   return hipGetLastError();
@@ -433,7 +461,7 @@ hipError_t launch_zero_dropped(const Layer& ly, const int32_t* offsets, const in
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
                               const TileList& small_tiles, const TilePlan& plan, hipStream_t s) {
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, nullptr, offsets, nullptr,
-                     ly.E, plan, tiles, small_tiles, 0, nullptr);
+                     ly.E, plan, tiles, small_tiles, 0, nullptr, nullptr, int64_t(0));
   return hipGetLastError();
 }
 
