@@ -47,7 +47,7 @@ extern "C" {
 #define MOE_API
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 16
 
@@ -208,6 +208,26 @@ MOE_API moe_status_t moe_workspace_size(const moe_config_t* cfg, int64_t num_tok
 MOE_API moe_status_t moe_forward(const moe_config_t* cfg, const moe_weights_t* weights, int64_t num_tokens,
                          const void* x, void* y, moe_routing_t* routing, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* Device memory of moe_forward_noalloc, per GPU (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and results, with
+ * the workspace taken from a library-owned array of MOE_NOALLOC_SCRATCH_BYTES on each GPU,
+ * held from the first call on that GPU until the process ends. The caller still passes the
+ * inputs, y and the optional routing outputs. The first call on a device looks up that
+ * device's copy of the array (with the device current); no call allocates or frees device
+ * memory. WORKSPACE_TOO_SMALL (nothing enqueued) when moe_workspace_size(cfg, T) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (decode-sized batches fit: 64 tokens of an 896-expert latent
+ * layer need 5.4 MiB). Every call on a GPU uses that GPU's one array: calls that overlap on
+ * one GPU (two streams, two threads) race and must be ordered by the caller. The array keeps
+ * the last call's contents; the forward reads nothing it did not write in the same call.
+ */
+MOE_API moe_status_t moe_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* weights,
+                                 int64_t num_tokens, const void* x, void* y, moe_routing_t* routing,
+                                 void* stream);
 
 /* ------------------------------------------------------------------------ stage calls */
 

@@ -111,6 +111,9 @@ int main(void) {
   EXPECT(moe_workspace_size(&c, T, &ws) == MOE_OK);
   EXPECT(moe_forward(&c, &w, T, fake, fake, nullptr, fake, ws - 1, nullptr) == MOE_ERR_WORKSPACE_TOO_SMALL);
   EXPECT(moe_forward(&c, &w, 0, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == MOE_OK);
+  EXPECT(moe_forward_noalloc(&c, &w, 8192, fake, fake, nullptr, nullptr) == MOE_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(moe_forward_noalloc(&c, &w, T, nullptr, fake, nullptr, nullptr) == MOE_ERR_INVALID_ARG);
+  EXPECT(moe_forward_noalloc(nullptr, &w, T, fake, fake, nullptr, nullptr) == MOE_ERR_INVALID_ARG);
   moe_routing_t r;
   memset(&r, 0, sizeof r);
   EXPECT(moe_router_forward(&c, &w, T, fake, &r, fake, ws, nullptr) == MOE_ERR_INVALID_ARG);

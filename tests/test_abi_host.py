@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_declares_the_abi():
     syms = declared_symbols()
-    for name in ("moe_forward", "moe_router_forward", "moe_route_from_scores", "moe_permute",
+    for name in ("moe_forward", "moe_forward_noalloc", "moe_router_forward", "moe_route_from_scores", "moe_permute",
                  "moe_experts_forward", "moe_combine", "moe_latent_down", "moe_latent_up",
                  "moe_config_default", "moe_config_validate", "moe_num_params",
                  "moe_workspace_size", "moe_status_string", "moe_last_error_message",
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_size():
-    assert moe.abi_version() == 6
+    assert moe.abi_version() == 7
     c = moe._CConfig()
     assert moe._config_default(ctypes.byref(c)) == 0
     assert c.struct_size == ctypes.sizeof(moe._CConfig)
@@ -146,6 +146,26 @@ def test_forward_argument_errors_before_any_gpu_call():
     assert moe._latent_down(ctypes.byref(lat), ctypes.byref(wl), T, fake, fake, fake, need_l - 1, None) == 3
     assert moe._latent_up(ctypes.byref(lat), ctypes.byref(wl), T, fake, fake, fake, need_l - 1, None) == 3
     assert moe._permute(ctypes.byref(c), T, fake, fake, fake, fake, fake, fake, 16, None) == 3
+
+
+def test_forward_noalloc_errors_before_any_gpu_call():
+    """The allocation-free forward checks its arguments and the scratch size on the host: a
+    layer whose workspace exceeds MOE_NOALLOC_SCRATCH_BYTES is refused before any HIP call."""
+    cfg = moe.MoEConfig.of(workloads.layer_config("olmoe"))
+    c = cfg.to_c()
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails on the host
+    w = moe._CWeights()
+    T = 8192
+    assert moe.workspace_size(cfg, T) > moe.NOALLOC_SCRATCH_BYTES
+    assert moe._forward_noalloc(ctypes.byref(c), None, T, fake, fake, None, None) == 1
+    w.router_weight = w.w1 = w.w2 = fake
+    assert moe._forward_noalloc(ctypes.byref(c), ctypes.byref(w), T, None, fake, None, None) == 1
+    assert moe._forward_noalloc(ctypes.byref(c), ctypes.byref(w), T, fake, None, None, None) == 1
+    assert moe._forward_noalloc(ctypes.byref(c), ctypes.byref(w), T, fake, fake, None, None) == 3
+    msg = moe._last_error().decode()
+    assert "allocation-free" in msg and str(moe.NOALLOC_SCRATCH_BYTES) in msg
+    assert moe._forward_noalloc(ctypes.byref(c), ctypes.byref(w), 0, None, None, None, None) == 0
+    assert moe._forward_noalloc(None, ctypes.byref(w), T, fake, fake, None, None) == 1
 
 
 def test_balancing_entry_points_validate_before_any_gpu_call():

@@ -80,6 +80,9 @@ _workspace_size = _sig("moe_workspace_size", c_i32, _P(_CConfig), c_i64, _P(ctyp
 _expert_capacity = _sig("moe_expert_capacity", c_i32, _P(_CConfig), c_i64, _P(c_i64))
 _forward = _sig("moe_forward", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp,
                 _P(_CRouting), c_vp, ctypes.c_size_t, c_vp)
+_forward_noalloc = _sig("moe_forward_noalloc", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp, c_vp,
+                        _P(_CRouting), c_vp)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 _router_forward = _sig("moe_router_forward", c_i32, _P(_CConfig), _P(_CWeights), c_i64, c_vp,
                        _P(_CRouting), c_vp, ctypes.c_size_t, c_vp)
 _route_from_scores = _sig("moe_route_from_scores", c_i32, _P(_CConfig), c_i64, c_vp, c_vp, c_vp,
@@ -331,6 +334,17 @@ class MoELayer:
         return (y, r) if want else y
 
     __call__ = forward
+
+    def forward_noalloc(self, x: torch.Tensor, out: torch.Tensor, routing: Optional[dict] = None) -> None:
+        """y = layer(x) into `out` through moe_forward_noalloc: the library's per-GPU scratch
+        array is the workspace, and nothing is allocated (routing: an optional dict of
+        preallocated ROUTING_FIELDS tensors to fill)."""
+        T = x.shape[0]
+        _expect(x, (T, self.cfg.d_model), self.cfg.torch_dtype, "x")
+        _expect(out, (T, self.cfg.d_model), self.cfg.torch_dtype, "out")
+        cr = _c_routing(routing) if routing else None
+        _check(_forward_noalloc(ctypes.byref(self._c), ctypes.byref(self._cw), T, _ptr(x), _ptr(out),
+                                ctypes.byref(cr) if cr is not None else None, _stream()))
 
 
 # --------------------------------------------------------------------------- stage calls

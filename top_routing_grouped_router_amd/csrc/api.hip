@@ -16,6 +16,11 @@
 
 #include "common.hpp"
 
+// Device memory of moe_forward_noalloc: the forward's workspace for callers that cannot
+// allocate. One copy per GPU, held until the process ends; host code uses the per-device
+// address from hipGetSymbolAddress, never this name (the name is a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace moe {
 
 namespace {
@@ -785,6 +790,27 @@ moe_status_t enqueue_forward(const Layer& ly, const WsLayout& L, const moe_weigh
   return ok();
 }
 
+// Address of `scratch` on each device, looked up once per device (with that device current)
+// on the first allocation-free call there. A fixed table: the lookup allocates nothing.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+moe_status_t noalloc_scratch(void** out) {
+  int dev = 0;
+  MOE_TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device ordinal beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    MOE_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -800,6 +826,23 @@ moe_status_t moe_forward(const moe_config_t* c, const moe_weights_t* w, int64_t 
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
                                                  std::to_string(L.total));
+  return enqueue_forward(ly, L, w, x, y, routing, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_forward_noalloc(const moe_config_t* c, const moe_weights_t* w, int64_t T, const void* x, void* y,
+                                 moe_routing_t* routing, void* stream) {
+  moe_status_t st = check_forward(c, w, T, x, y);
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  const Layer ly = make_layer(c, T);
+  const WsLayout L = ws_layout(ly);
+  if (L.total > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "this layer needs " + std::to_string(L.total) + " bytes of workspace for " + std::to_string(T) +
+                    " tokens; the allocation-free forward holds " + std::to_string(MOE_NOALLOC_SCRATCH_BYTES) +
+                    ": use moe_forward with a caller workspace, or fewer tokens per call");
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != MOE_OK) return st;
   return enqueue_forward(ly, L, w, x, y, routing, ws, static_cast<hipStream_t>(stream));
 }
 
