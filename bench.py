@@ -59,11 +59,20 @@ def parse():
                     help="skip the extra measurement of the routed experts' backward")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the measurement of the achievable matrix-core and copy rates")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor BLAS (torch linear, hipBLASLt) on one expert's dense GEMM "
+                         "shapes of the headline workload (context for the grouped GEMM's rate)")
     ap.add_argument("--profile-run", action="store_true",
                     help="only run --warmup + --steps layer forwards of --workload (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference the HBM "
                          "byte counters are scaled by")
+    ap.add_argument("--restage-traffic", metavar="JSON",
+                    help="no GPU: recompute the stage sums of a traffic record from its per-kernel entries "
+                         "(with this file's stage classification) and write it to profiles/")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="no GPU: print, per kernel of a rocprofv3 --pmc output folder, the dispatches, the "
+                         "mean duration and the mean of each counter (one JSON line per kernel)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="no GPU: write profiles/traffic_<workload>.json from four rocprofv3 --pmc output "
                          "folders (FETCH_SIZE and WRITE_SIZE of --profile-run, then of --copy-calibration 256)")
@@ -112,7 +121,9 @@ def kernel_stage(name):
     if "gemm_skinny" in name:
         return "latent"
     if "gemm_bf16_kernel" in name:
-        if "ShapeRouter" in name:
+        # Shape<WM, WN, TM, TN, BK, NSTAGE, WG_PER_CU, PLANES, ...>: three weight planes = router
+        shape = name.split("Shape<", 1)[1].split(">", 1)[0].split(",") if "Shape<" in name else []
+        if "ShapeRouter" in name or (len(shape) > 7 and shape[7].strip() == "3"):
             return "router"
         f = _gemm_flags(name)
         if f[:3] == ["true", "true", "false"] or f[:3] == ["false", "false", "true"]:
@@ -133,6 +144,37 @@ def _counter_rows(folder):
         raise SystemExit(f"no counter_collection.csv under {folder}")
     with open(files[0]) as f:
         return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
+
+
+def counter_summary(folder):
+    """Per kernel of a rocprofv3 --pmc csv folder: dispatches, mean duration (ns) and the mean of
+    each counter per dispatch; derived for the clock and matrix-core counters: the shader clock
+    (GRBM_GUI_ACTIVE over the 8 XCDs / duration) and the matrix-core busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs / the active cycles of one XCD)."""
+    import csv
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    agg = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            k = agg.setdefault(r["Kernel_Name"], {"dispatch": set(), "dur": {}, "ctr": {}})
+            d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            k["dispatch"].add(d)
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                k["dur"][d] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            k["ctr"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for name, k in agg.items():
+        n = len(k["dispatch"])
+        rec = {"kernel": name, "stage": kernel_stage(name), "dispatches": n,
+               "mean_ns": round(sum(k["dur"].values()) / len(k["dur"]), 1) if k["dur"] else None}
+        for cn, vals in k["ctr"].items():
+            rec[cn] = sum(vals) / len(vals)
+        if rec["mean_ns"] and "GRBM_GUI_ACTIVE" in rec:
+            rec["clock_ghz"] = round(rec["GRBM_GUI_ACTIVE"] / 8 / rec["mean_ns"], 3)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in rec:
+                rec["mfma_busy"] = round(rec["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (rec["GRBM_GUI_ACTIVE"] / 8), 4)
+        print(json.dumps(rec))
 
 
 def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, steps, copy_mib=256):
@@ -190,6 +232,32 @@ def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps({"workload": workload, "stages": stages}))
+
+
+def restage_traffic(path):
+    """Stage sums of a traffic record from its per-kernel entries, classified by kernel_stage;
+    the stage source hashes are kept from the record where the stage existed (they describe the
+    sources the counters were taken on), else taken from the current sources."""
+    with open(path) as f:
+        rec = json.load(f)
+    old = rec.get("stages", {})
+    stages = {}
+    for name, k in rec["kernels"].items():
+        st = kernel_stage(name)
+        k["stage"] = st
+        if st is None:
+            continue
+        s = stages.setdefault(st, {"fetch_bytes": 0.0, "write_bytes": 0.0})
+        s["fetch_bytes"] += k["fetch_bytes_per_step"]
+        s["write_bytes"] += k["write_bytes_per_step"]
+    for st, s in stages.items():
+        s["bytes"] = int(round(s["fetch_bytes"] + s["write_bytes"]))
+        s["source_sha256"] = old.get(st, {}).get("source_sha256") or sources_sha256(STAGE_SOURCES[st])
+    rec["stages"] = stages
+    out = os.path.join(ROOT, "profiles", f"traffic_{rec['workload']}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"workload": rec["workload"], "stages": stages}))
 
 
 def recorded_stage_traffic(workload):
@@ -467,6 +535,32 @@ def measure_layer(moe, torch, name, cfg, w, x, steps, warmup, flush_buf, precisi
     return out
 
 
+def vendor_dense_gemm(cfg, w, rows, torch, reps=10):
+    """The vendor BLAS (torch.nn.functional.linear on bf16: hipBLASLt) on the dense shapes of
+    the busiest expert: M = its rows, GEMM1 (M, K) x (2h, K)^T and GEMM2 (M, h) x (K, h)^T, on
+    random rows. Context for the grouped kernels' rate (which also gather, scatter and fuse
+    SwiGLU); not part of the layer."""
+    import torch.nn.functional as F
+    h = cfg["hidden_size"]
+    K = cfg["latent_dim"] or cfg["d_model"]
+    e = int(torch.argmax(rows))
+    M = int(rows[e])
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a1 = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+    a2 = torch.randn((M, h), generator=g, device="cuda").to(torch.bfloat16)
+    w1, w2 = w["w1"][e].contiguous(), w["w2"][e].contiguous()
+    for _ in range(2):
+        F.linear(a1, w1)
+        F.linear(a2, w2)
+    t1 = pstats(event_times_ms(lambda: F.linear(a1, w1), reps, torch))["median"]
+    t2 = pstats(event_times_ms(lambda: F.linear(a2, w2), reps, torch))["median"]
+    f1, f2 = 2.0 * M * 2 * h * K, 2.0 * M * K * h
+    return {"what": "torch.nn.functional.linear (hipBLASLt), bf16, the busiest expert's dense shapes",
+            "rows": M, "gemm1_ms": round(t1, 4), "gemm1_tflops": round(f1 / (t1 / 1e3) / 1e12, 1),
+            "gemm2_ms": round(t2, 4), "gemm2_tflops": round(f2 / (t2 / 1e3) / 1e12, 1),
+            "pair_tflops": round((f1 + f2) / ((t1 + t2) / 1e3) / 1e12, 1)}
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 def host_description():
@@ -538,6 +632,12 @@ def main():
     args = parse()
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic, steps=args.warmup + args.steps)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.restage_traffic:
+        restage_traffic(args.restage_traffic)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -665,6 +765,12 @@ def main():
             mxr = out["mxfp8_experts"]
             mxr["achievable_peak_tflops"] = cal["mfma_mxfp8_tflops"]
             mxr["frac_of_achievable"] = round(mxr["achieved_tflops"] / cal["mfma_mxfp8_tflops"], 4)
+    if args.vendor_gemm and cfg["dtype"] == "bf16":
+        layer = moe.MoELayer(cfg, w)
+        _, r = layer(x, routing=("batch_size_per_expert",))
+        out["vendor_dense_gemm"] = vendor_dense_gemm(cfg, w, r["batch_size_per_expert"], torch)
+        del layer, r
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, x, args.cpu_seconds)
     del w, x
