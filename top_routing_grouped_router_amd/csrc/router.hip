@@ -69,7 +69,9 @@ struct GateArgs {
   int orig_k;
 };
 
-template <int GATING, bool FROM_SCORES, int PL>
+// MULTI: the input has split-K partial-sum planes to add (compiled out otherwise: the plane
+// batches hold registers).
+template <int GATING, bool FROM_SCORES, int PL, bool MULTI>
 __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   float v[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) v[i] = row[min(i * kWave + lane, E - 1)];
-  constexpr int PB = PL >= 8 ? 2 : 4;  // planes per batch
-  for (int p0 = 1; p0 < a.nsplit; p0 += PB) {
+  constexpr int PB = 4;  // planes per batch (each batch's loads are issued together)
+  for (int p0 = 1; MULTI && p0 < a.nsplit; p0 += PB) {
     float pv[PB][PL];
 #pragma unroll
     for (int u = 0; u < PB; ++u)
@@ -261,21 +263,22 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
   }
 }
 
-template <int GATING, bool FS>
+template <int GATING, bool FS, bool MULTI>
 void launch_gate_pl(const GateArgs& a, hipStream_t s) {
   const dim3 g(static_cast<unsigned>((a.T + 3) / 4)), b(256);
   const int per_lane = (a.E + kWave - 1) / kWave;
-  if (per_lane <= 1) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 1>), g, b, 0, s, a);
-  else if (per_lane <= 2) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 2>), g, b, 0, s, a);
-  else if (per_lane <= 4) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 4>), g, b, 0, s, a);
-  else if (per_lane <= 8) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 8>), g, b, 0, s, a);
-  else hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, kMaxSlots>), g, b, 0, s, a);
+  if (per_lane <= 1) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 1, MULTI>), g, b, 0, s, a);
+  else if (per_lane <= 2) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 2, MULTI>), g, b, 0, s, a);
+  else if (per_lane <= 4) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 4, MULTI>), g, b, 0, s, a);
+  else if (per_lane <= 8) hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, 8, MULTI>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((gate_topk_kernel<GATING, FS, kMaxSlots, MULTI>), g, b, 0, s, a);
 }
 
 template <int GATING>
 void launch_gate(const GateArgs& a, bool from_scores, hipStream_t s) {
-  if (from_scores) launch_gate_pl<GATING, true>(a, s);
-  else launch_gate_pl<GATING, false>(a, s);
+  if (from_scores) launch_gate_pl<GATING, true, false>(a, s);
+  else if (a.nsplit > 1) launch_gate_pl<GATING, false, true>(a, s);
+  else launch_gate_pl<GATING, false, false>(a, s);
 }
 
 // ------------------------------------------------------------------ router logits on MFMA
