@@ -272,3 +272,16 @@ def test_calibration_entry_points_validate_before_any_gpu_call():
         assert moe._calibrate_copy(fake, fake, nbytes, None) == 1
     assert moe._calibrate_copy(None, fake, 64, None) == 1
     assert moe._calibrate_copy(fake, None, 64, None) == 1
+
+
+def test_router_weight_planes_beyond_4gib_are_refused():
+    # The large-layer router splits the fp32 router weights into three bf16 planes addressed
+    # with 32-bit byte offsets: 3 * E * d_model elements of 2 bytes must stay below 4 GiB.
+    ok = dict(workloads.layer_config("latent896"), num_experts=1024, d_model=698048, latent_dim=64)
+    assert 3 * 1024 * 698048 < (1 << 31)
+    assert moe.workspace_size(ok, 1) > 0
+    big = dict(ok, d_model=699072)
+    assert 3 * 1024 * 699072 >= (1 << 31)
+    with pytest.raises(moe.MoEError) as e:
+        moe.workspace_size(big, 1)
+    assert e.value.status == 2 and "4 GiB" in str(e.value)

@@ -161,8 +161,9 @@ moe_status_t check_tokens(const moe_config_t* c, int64_t T) {
     const int64_t K = c->latent_dim ? c->latent_dim : c->d_model;
     const int64_t A = T * c->top_k;
     const int64_t lim = int64_t(1) << 31;  // elements of 2 bytes
+    // (3 * E * d: the router weights split into three bf16 planes for the large-layer router)
     if (T * c->d_model >= lim || T * K >= lim || A * c->hidden_size >= lim || A * K >= lim ||
-        2 * c->hidden_size * K >= lim || c->d_model * K >= lim)
+        2 * c->hidden_size * K >= lim || c->d_model * K >= lim || 3 * c->num_experts * c->d_model >= lim)
       return fail(MOE_ERR_UNSUPPORTED, "a bf16 GEMM operand would exceed 4 GiB; split the batch");
   }
   return MOE_OK;
