@@ -292,6 +292,7 @@ __device__ void block_exclusive_scan_e(const int32_t* v, int E, int32_t* out, in
 // in order and ranks each copy like rank_kernel (64-bit per-wavefront masks), on top of the
 // running count of its expert from the earlier chunks.
 constexpr int kSmallTokens = 1024;
+constexpr int kMaxTopK = MOE_MAX_TOP_K;  // entries per token (top_k is validated against it)
 
 __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ idx, int64_t T, int k,
                                                              int E, int32_t* __restrict__ counts,
@@ -316,13 +317,21 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
 
   for (int e = tid; e < E; e += 256) run[e] = 0;
   __syncthreads();
-  for (int64_t a = tid; a < A; a += 256) {
-    const int e = idx[a];
-    if (e < 0 || e >= E) continue;
-    const int64_t row = a - a % k;
-    bool repeat = false;
-    for (int64_t q = row; q < a; ++q) repeat |= idx[q] == e;
-    if (!repeat) atomicAdd(&run[e], 1);
+  // Each token's k entries are read once, as independent loads, and kept in registers; an
+  // entry repeating an earlier expert of its token is not counted.
+  for (int64_t t = tid; t < T; t += 256) {
+    int ek[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) ek[j] = j < k ? idx[t * k + j] : -1;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int e = ek[j];
+      if (j >= k || e < 0 || e >= E) continue;
+      bool repeat = false;
+#pragma unroll
+      for (int q = 0; q < j; ++q) repeat |= ek[q] == e;
+      if (!repeat) atomicAdd(&run[e], 1);
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
@@ -368,10 +377,14 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     __syncthreads();
     const int64_t t = t0 + tid;
     uint32_t rep = 0;  // bit j: entry j repeats an earlier expert of the token
+    int ek[kMaxTopK];  // the token's entries, read once
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) ek[j] = (t < T && j < k) ? idx[t * k + j] : -1;
     if (t < T) {
-      for (int j = 0; j < k; ++j) {
-        const int e = idx[t * k + j];
-        if (e >= 0 && e < E) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        const int e = ek[j];
+        if (j < k && e >= 0 && e < E) {
           const unsigned long long old =
               atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]), 1ull << lane);
           if (old & (1ull << lane)) rep |= 1u << j;
@@ -390,9 +403,11 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     }
     __syncthreads();
     if (t < T) {
-      for (int j = 0; j < k; ++j) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j >= k) break;
         const int64_t a = t * k + j;
-        const int e = idx[a];
+        const int e = ek[j];
         if (e < 0 || e >= E || ((rep >> j) & 1u)) {
           inv[a] = -1;
           continue;
