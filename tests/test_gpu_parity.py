@@ -117,6 +117,15 @@ def test_permute_zero_tokens():
     torch.cuda.synchronize()
     assert int(r["batch_size_per_expert"].abs().sum()) == 0
     assert int(r["expert_offsets"].abs().sum()) == 0
+    # the histogram of an empty batch is written, whatever the buffers held (E = 300: a grid of
+    # two blocks for the 301 offsets)
+    c = moe.MoEConfig.of(dict(cfg, num_experts=300)).to_c()
+    counts = torch.full((300,), 77, dtype=torch.int32, device="cuda")
+    offsets = torch.full((301,), -5, dtype=torch.int32, device="cuda")
+    assert moe._permute(ctypes.byref(c), 0, None, moe._ptr(counts), moe._ptr(offsets), None, None, None, 0,
+                        moe._stream()) == 0
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
 
 
 def _expected_dispatch(idx, E, capacity):

@@ -902,8 +902,7 @@ moe_status_t moe_permute(const moe_config_t* c, int64_t T, const int32_t* idx, i
   const Layer ly = make_layer(c, T);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {  // no assignments: permutation buffers are empty (may be NULL)
-    MOE_TRY_HIP(hipMemsetAsync(counts, 0, sizeof(int32_t) * ly.E, s), "zero counts");
-    MOE_TRY_HIP(hipMemsetAsync(offsets, 0, sizeof(int32_t) * (ly.E + 1), s), "zero offsets");
+    MOE_TRY_HIP(launch_zero_counts_offsets(counts, offsets, ly.E, s), "zero counts and offsets");
     return ok();
   }
   if ((st = need(perm, "permutation")) != MOE_OK) return st;

@@ -321,6 +321,8 @@ hipError_t launch_sum_copies(const Layer& ly, const void* in, void* out, hipStre
 hipError_t launch_combine_backward(const Layer& ly, const void* y_assign, const float* w, const void* d_out,
                                    void* dy_assign, float* dw, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// counts (E) and offsets (E + 1) set to zero (an empty batch's histogram)
+hipError_t launch_zero_counts_offsets(int32_t* counts, int32_t* offsets, int E, hipStream_t s);
 // order (E): the experts by decreasing row count offsets[e+1] - offsets[e], ties by index
 // (E <= 1024).
 hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order, hipStream_t s);

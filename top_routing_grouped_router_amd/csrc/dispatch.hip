@@ -473,6 +473,24 @@ hipError_t launch_zero_dropped(const Layer& ly, const int32_t* offsets, const in
   return hipGetLastError();
 }
 
+namespace {
+// counts (E) and offsets (E + 1) of an empty batch, zeroed by a kernel rather than memset nodes so
+// that a caller may capture the call in a graph.
+__global__ __launch_bounds__(256) void zero_counts_offsets_kernel(int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets, int E) {
+  for (int e = blockIdx.x * 256 + threadIdx.x; e <= E; e += gridDim.x * 256) {
+    if (e < E) counts[e] = 0;
+    offsets[e] = 0;
+  }
+}
+}  // namespace
+
+hipError_t launch_zero_counts_offsets(int32_t* counts, int32_t* offsets, int E, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counts_offsets_kernel, dim3(static_cast<unsigned>((E + 256) / 256)), dim3(256), 0, s,
+                     counts, offsets, E);
+  return hipGetLastError();
+}
+
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
                               const TileList& small_tiles, const TilePlan& plan, hipStream_t s) {
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, nullptr, offsets, nullptr,
