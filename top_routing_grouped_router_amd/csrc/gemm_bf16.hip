@@ -225,6 +225,31 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int col32, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The same directives with a stage's KLOADS global->LDS loads placed as one group: before step 0's
+// LDS reads (AT < 0) or right after the MFMAs of k16 step AT.
+template <int KK, int KSTEPS, int KREADS, int KMFMA, int KLOADS, int AT>
+__device__ __forceinline__ void sched_stage_loads_at_step() {
+  if constexpr (KK < KSTEPS) {
+    constexpr int reads = (KK + 1 < KSTEPS) ? KREADS : 0;
+    constexpr int r1 = reads < KMFMA ? reads : KMFMA;
+#pragma unroll
+    for (int q = 0; q < r1; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (reads > r1) __builtin_amdgcn_sched_group_barrier(0x100, reads - r1, 0);
+    if constexpr (KMFMA - r1 > 0) __builtin_amdgcn_sched_group_barrier(0x008, KMFMA - r1, 0);
+    if constexpr (KK == AT) __builtin_amdgcn_sched_group_barrier(0x010, KLOADS, 0);
+    sched_stage_loads_at_step<KK + 1, KSTEPS, KREADS, KMFMA, KLOADS, AT>();
+  }
+}
+template <int KSTEPS, int KREADS, int KMFMA, int KLOADS, int AT>
+__device__ __forceinline__ void sched_stage_loads_at() {
+  if constexpr (AT < 0) __builtin_amdgcn_sched_group_barrier(0x010, KLOADS, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);  // step-0 reads
+  sched_stage_loads_at_step<0, KSTEPS, KREADS, KMFMA, KLOADS, AT>();
+}
+
 template <int KSTEPS, int KREADS, int KMFMA, int KLOADS>
 __device__ __forceinline__ void sched_stage() {
   __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);  // step-0 reads
@@ -635,6 +660,10 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // wavefront issues exactly NQ operand loads (plus one scale load for MXFP8 wavefronts below
   // NSC), the count the scatter wait below relies on. Other shapes issue it in the last round.
   constexpr bool EARLY = !WGRAD && !S::MX && S::BM == 256 && S::NI % S::NW == 0;
+  // Large row-major tiles stagger their loads (see the k-loop): every k-stage issues its loads,
+  // the last one of a tile reloading its own stage into the free slot, so the epilogue first
+  // waits for those before it reuses a slot.
+  constexpr bool STAGGER = EARLY && BUF;
   constexpr int NSIDX = SCATTER ? (EARLY ? NR * KI : KI) : 1;
   auto epilogue = [&](const TileState& t, bool more, const TileFetch& fn, int64_t it_next, TileState& nx) {
     // The thread index passes through an empty asm statement: the epilogue's per-lane addresses
@@ -655,6 +684,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         sidx[base + k] = c.scatter[min(t.row0 + (m < t.rows ? m : 0), c.rows_bound - 1)];
       }
     };
+    if constexpr (STAGGER) wait_vmcnt<0>();
     if constexpr (SCATTER && EARLY) {
 #pragma unroll
       for (int rho = 0; rho < NR; ++rho) load_sidx(rho, rho * KI);
@@ -881,16 +911,11 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int64_t it_pre = it + per_xcd;
     const bool fetch_next = EARLY && it_pre < chunk && xcd * chunk + it_pre < total;
     if (fetch_next && nk <= 0) fetch(it_pre, fnext);
-    // Stage kt reads slot `la` (lds0 for even kt, lds1 for odd) and refills the other one; the
-    // loop runs two stages per iteration so that each stage's slot is known at compile time.
-    auto kstage = [&](int kt, const unsigned char* la, unsigned char* other) {
-      // This wavefront's loads of stage kt have landed; after the barrier so have every
-      // wavefront's, and every wavefront is done reading stage kt-1, whose slot is refilled.
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
+    // The MFMA work of k-stage kt from slot `la`, with its scheduling directives. late
+    // (staggered loads, see the k-loop below): this wavefront's loads of the stage come after
+    // its first k16 step instead of before its first LDS reads.
+    auto stage_compute = [&](int kt, const unsigned char* la, auto late) __attribute__((always_inline)) {
       const unsigned char* lb = la + S::BM * S::ROWB;
-      if (kt + 1 < nk) issue(cur, kt + 1, other);
-      if (fetch_next && kt == 0) fetch(it_pre, fnext);
       // k16 steps with fragments double-buffered in registers; the directives interleave step
       // kk+1's LDS reads with step kk's MFMAs so the matrix pipe does not wait on an LDS round
       // trip before every MFMA group.
@@ -927,12 +952,57 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
               for (int pl = S::PLANES - 1; pl >= 0; --pl)  // smallest plane first
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk & 1][pl][j], ft[kk & 1][i], acc[i][j], 0, 0, 0);
         }
-        sched_stage<kSteps, kReads, kMfma, 0>();
+        if constexpr (STAGGER)
+          sched_stage_loads_at<kSteps, kReads, kMfma, S::NQ, decltype(late)::value ? 0 : -1>();
+        else
+          sched_stage<kSteps, kReads, kMfma, 0>();
       }
     };
-    for (int kt = 0; kt < nk; kt += 2) {
-      kstage(kt, lds0, lds1);
-      if (kt + 1 < nk) kstage(kt + 1, lds1, lds0);
+    // Stage kt reads slot `la` (lds0 for even kt, lds1 for odd) and refills the other one; the
+    // loop runs two stages per iteration so that each stage's slot is known at compile time.
+    auto kstage = [&](int kt, const unsigned char* la, unsigned char* other) {
+      // This wavefront's loads of stage kt have landed; after the barrier so have every
+      // wavefront's, and every wavefront is done reading stage kt-1, whose slot is refilled.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + 1 < nk) issue(cur, kt + 1, other);
+      if (fetch_next && kt == 0) fetch(it_pre, fnext);
+      stage_compute(kt, la, std::false_type{});
+    };
+    // The same with staggered loads: every stage issues its loads unconditionally, so they sit in
+    // the MFMAs' block where the directives place them; the last stage of a tile reloads its own
+    // stage into the free slot (valid addresses, never read), which the epilogue waits for.
+    auto kstage_staggered = [&](int kt, const unsigned char* la, unsigned char* other, auto late)
+                                __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      issue(cur, kt + 1 < nk ? kt + 1 : kt, other);
+      stage_compute(kt, la, late);
+      if (fetch_next && kt == 0) fetch(it_pre, fnext);
+    };
+    // A stage's 64 loads issued as one burst right after the barrier fill the address unit's
+    // queues, and a wavefront stalls on issue before it reaches its MFMAs. With STAGGER the two
+    // wavefronts of a SIMD (w and w + 4) split: the first half issues at the stage start, the
+    // second after its first k16 step, so one of each pair computes while the other's loads
+    // queue. (Same-box A/B, outputs bitwise equal: skewed layer 11.90 -> 11.58 ms, olmoe -2 %,
+    // latent896 -1 %; the second half one step later, or its loads interleaved with the MFMAs,
+    // measured slower.)
+    if constexpr (STAGGER) {
+      auto kloop = [&](auto late) __attribute__((always_inline)) {
+        for (int kt = 0; kt < nk; kt += 2) {
+          kstage_staggered(kt, lds0, lds1, late);
+          if (kt + 1 < nk) kstage_staggered(kt + 1, lds1, lds0, late);
+        }
+      };
+      if (wave >= S::NW / 2)
+        kloop(std::true_type{});
+      else
+        kloop(std::false_type{});
+    } else {
+      for (int kt = 0; kt < nk; kt += 2) {
+        kstage(kt, lds0, lds1);
+        if (kt + 1 < nk) kstage(kt + 1, lds1, lds0);
+      }
     }
     // Every wavefront done reading this tile's last stages: slot 0 is free for the next tile.
     // (Weight-gradient mode: a full workgroup barrier with fences, which also publishes the
