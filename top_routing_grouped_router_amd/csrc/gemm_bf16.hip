@@ -31,6 +31,9 @@
 //     through a buffer descriptor per operand, the k-stage step a scalar offset; measured on
 //     the same box, that streams faster than global_load_lds (a 32768 x 4096 x 4096 dense
 //     product 1191 -> 1248 TFLOP/s), and the operand loads need no per-lane 64-bit addresses.
+//   * Staggered load issue (large row-major tiles): of the two wavefronts sharing a SIMD, one
+//     issues its share of the next stage's loads before its first fragment reads, the other
+//     after its first k16 step, so the pair does not stall together on a full address queue.
 //   * Epilogue through LDS: the accumulators leave the MFMA layout as 8-byte pieces of 32
 //     different rows, so stored directly every instruction writes 32 partial lines. They are
 //     staged in the free ring slot instead and stored as whole rows (full 128-byte lines per
