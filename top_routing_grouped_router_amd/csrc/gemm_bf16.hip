@@ -25,7 +25,8 @@
 //   * Persistent grid (one workgroup per CU slot). Workgroup i runs on XCD i % 8; the linear
 //     tile sequence is cut into 8 contiguous chunks, one per XCD, and inside a chunk tiles go
 //     in groups of 4 M-tiles x all N-tiles, so the tiles an XCD runs together share A and B
-//     panels in that XCD's L2.
+//     panels in that XCD's L2. Small tiles use only as many workgroups of an XCD as finish its
+//     chunk in the same number of rounds, so no round runs part-empty.
 //   * Operands reach LDS by DMA (16 bytes per lane, no register round trip); each 64-k stage
 //     is one whole 128-byte line per staged row. Row-major operands use buffer_load ... lds
 //     through a buffer descriptor per operand, the k-stage step a scalar offset; measured on
@@ -311,8 +312,17 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
                                                 static_cast<int64_t>(c.tiles.cap));
   const int64_t total = total_m * ntn;
   const int xcd = blockIdx.x % kXcds;
-  const int per_xcd = gridDim.x / kXcds;
   const int64_t chunk = (total + kXcds - 1) / kXcds;
+  // Small tiles stream weights from HBM, and a last round that only part of the workgroups
+  // run leaves bandwidth unused: there only as many workgroups of the XCD take part as still
+  // finish its chunk in the same number of rounds, each taking the same number of tiles.
+  // (Large tiles are bound by the matrix cores, where the slowest workgroup's tile count
+  // decides either way.)
+  int per_xcd = gridDim.x / kXcds;
+  if constexpr (!WGRAD && S::WG_PER_CU > 1) {
+    const int64_t rounds = (chunk + per_xcd - 1) / per_xcd;
+    if (rounds > 0) per_xcd = static_cast<int>((chunk + rounds - 1) / rounds);
+  }
   const unsigned char* Ab = static_cast<const unsigned char*>(c.A);
   // bytes from one k-stage to the next: along the row, or 64 rows down for a contraction-major
   // operand
@@ -894,7 +904,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     __syncthreads();
   }
   int64_t it = WGRAD ? static_cast<int64_t>(sched[0]) : blockIdx.x / kXcds;
-  if (WGRAD ? it >= total : (it >= chunk || xcd * chunk + it >= total)) return;
+  if (WGRAD ? it >= total : (it >= chunk || it >= per_xcd || xcd * chunk + it >= total)) return;
   int parity = 1;
   TileFetch fnext;
   TileState cur;
