@@ -7,16 +7,16 @@
 // at most 64 tokens, so the bound is HBM and the work has to be spread over the whole chip.
 // Design:
 //   * A workgroup owns 64 weight rows x all (<= 64) token rows x one k-slice; the contraction
-//     is split over S workgroups (k-slices) and, inside a workgroup, over its 4 wavefronts.
-//   * No LDS staging of operands: each lane loads its v_mfma_f32_32x32x16_bf16 fragments
-//     straight from global memory. The order of k inside a 64-k block is permuted the same way
-//     for both operands (lane half h takes the 32 contiguous elements [32h, 32h + 32) of the
-//     block, 16 bytes per MFMA step), so each lane reads 64 contiguous bytes of a row and the
-//     two halves of a wavefront cover each row's whole 128-byte line.
-//   * The four wavefronts' fp32 tiles are added in LDS in wavefront order; with S = 1 the sum
-//     is rounded to bf16 and stored, otherwise it goes to fp32 partial plane `split`, and a
-//     second kernel adds the S planes in plane order and rounds. Fixed orders throughout, so
-//     results are bitwise reproducible.
+//     is split over S workgroups (k-slices), about 256 workgroups in all.
+//   * Operands reach LDS by DMA (buffer_load ... lds, 16 bytes per lane): each load fills 8
+//     rows x one 128-byte line of a 64-k stage, so every request is a whole line. 16-byte
+//     chunks are XOR-swizzled by row pair, so the fragment reads are free of bank conflicts.
+//     A four-slot ring keeps up to four stages (64 KiB) of a workgroup in flight.
+//   * Each of the 4 wavefronts owns a 32 x 32 block of the output (one
+//     v_mfma_f32_32x32x16_bf16 accumulator): weight half w & 1, token half w >> 1.
+//   * With S = 1 the block is rounded to bf16 and stored; otherwise it goes to fp32 partial
+//     plane `split`, and a second kernel adds the S planes in plane order and rounds. Fixed
+//     orders throughout, so results are bitwise reproducible.
 #include <algorithm>
 
 #include "common.hpp"
@@ -26,12 +26,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSkM = 64;     // token rows (padded)
-constexpr int kSkN = 64;     // weight rows per workgroup
-constexpr int kSkPad = 68;   // LDS row stride in floats: rows start 4 banks apart
+constexpr int kSkM = 64;      // token rows (padded)
+constexpr int kSkN = 64;      // weight rows per workgroup
 constexpr int kSkMaxSplit = 16;
+constexpr int kSkSlots = 4;   // ring depth (64-k stages)
+constexpr int kSkStage = (kSkM + kSkN) * 128;  // bytes per stage: 128 rows of 128 bytes
 
 struct SkinnyArgs {
   const uint16_t* A;  // (M, K) token rows
@@ -47,129 +47,135 @@ struct SkinnyArgs {
   int S;
 };
 
+#define SK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int N>
+__device__ __forceinline__ void sk_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// byte offset of logical 16-byte chunk c of staged row r
+__device__ __forceinline__ int sk_swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[4 * kSkM * kSkPad];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSkSlots * kSkStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kSkN;
   const int sp = blockIdx.y;
   const int nk = static_cast<int>(a.K / 64);
   const int kb = static_cast<int>(static_cast<int64_t>(sp) * nk / a.S);
-  const int ke = static_cast<int>(static_cast<int64_t>(sp + 1) * nk / a.S);
-  const int wb = kb + wave * (ke - kb) / 4, we = kb + (wave + 1) * (ke - kb) / 4;
+  const int ns = static_cast<int>(static_cast<int64_t>(sp + 1) * nk / a.S) - kb;  // stages of this slice
 
-  const int r = lane & 31, h = lane >> 5;
-  // Rows of this lane: weight rows n0 + 32u + r and token rows 32v + r (u, v = 0, 1), clamped
-  // into the operands; padded token rows compute values that are never stored.
-  const uint16_t* wrow[2];
-  const uint16_t* trow[2];
+  // Load q (0..3) of this wavefront fills staged rows [8i, 8i + 8), i = wave + 4q: token rows
+  // for i < 8, weight rows after. Lane: row 8i + lane / 8, LDS slot lane % 8, which holds the
+  // row's logical chunk (lane % 8) ^ ((row >> 1) & 7). Rows past the operand are clamped to its
+  // last row (their products are never stored).
+  uint32_t off[4];
+  bool is_a[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    wrow[u] = a.B + min(n0 + 32 * u + r, a.N - 1) * a.ldb + 32 * h;
-    trow[u] = a.A + min(static_cast<int64_t>(32 * u + r), a.M - 1) * a.lda + 32 * h;
+  for (int q = 0; q < 4; ++q) {
+    const int i = wave + 4 * q;
+    is_a[q] = i < 8;
+    const int r = (i & 7) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((r >> 1) & 7);
+    const int64_t row = is_a[q] ? min(static_cast<int64_t>(r), a.M - 1) : min(n0 + r, a.N - 1);
+    off[q] = static_cast<uint32_t>((row * (is_a[q] ? a.lda : a.ldb) + static_cast<int64_t>(kb) * 64) * 2 + ch * 16);
   }
+#if defined(__HIP_DEVICE_COMPILE__)
+  // uniform bases in scalar registers, widened from unsigned halves
+  auto rsrc = [](const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                                             static_cast<short>(0), -1, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t ra = rsrc(a.A), rb = rsrc(a.B);
+#endif
+  // stage s of the slice into ring slot s % kSkSlots (stages past the slice reload its last one)
+  auto issue = [&](int s) {
+    const int sc = min(s, ns - 1);
+    unsigned char* st = ring + (s % kSkSlots) * kSkStage;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a[q] ? ra : rb, SK_LDS(st + (wave + 4 * q) * 1024), 16, off[q],
+                                               static_cast<uint32_t>(sc) * 128, 0, 0);
+#endif
+    }
+  };
 
-  f32x16 acc[2][2];
+  f32x16 acc;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[u][v][q] = 0.f;
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  const int wr = 32 * (wave & 1) + (lane & 31);   // this lane's weight row in the tile
+  const int tr = 32 * (wave >> 1) + (lane & 31);  // this lane's token row
+  const int half = lane >> 5;
 
-  // Two 64-k blocks per iteration: 32 independent 16-byte loads per lane, then 16 MFMAs.
-  for (int kt = wb; kt < we; kt += 2) {
-    u32x4 fw[2][2][4], ft[2][2][4];
+  // Every wavefront issues exactly kSkSlots stages up front, then one per stage computed, so
+  // the count of loads still in flight after stage s's own is fixed: 4 per later stage issued.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int kk = min(kt + b, we - 1) * 64;  // a lone last block is loaded twice, used once
+  for (int s = 0; s < kSkSlots; ++s) issue(s);
+  for (int s = 0; s < ns; ++s) {
+    sk_wait_vmcnt<4 * (kSkSlots - 1)>();  // stage s landed (the kSkSlots - 1 later ones may not)
+    __builtin_amdgcn_s_barrier();
+    const unsigned char* st = ring + (s % kSkSlots) * kSkStage;
+    bf16x8 fw[4], ft[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          fw[b][u][s] = *reinterpret_cast<const u32x4*>(wrow[u] + kk + 8 * s);
-          ft[b][u][s] = *reinterpret_cast<const u32x4*>(trow[u] + kk + 8 * s);
-        }
+    for (int kk = 0; kk < 4; ++kk) {
+      fw[kk] = *reinterpret_cast<const bf16x8*>(st + kSkM * 128 + sk_swz(wr, 2 * kk + half));
+      ft[kk] = *reinterpret_cast<const bf16x8*>(st + sk_swz(tr, 2 * kk + half));
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (kt + b >= we) break;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int v = 0; v < 2; ++v)
-            acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fw[b][u][s]),
-                                                                __builtin_bit_cast(bf16x8, ft[b][v][s]),
-                                                                acc[u][v], 0, 0, 0);
-    }
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[kk], ft[kk], acc, 0, 0, 0);
+    // every wavefront has read slot s % kSkSlots before it is refilled
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    issue(s + kSkSlots);
   }
+  sk_wait_vmcnt<0>();  // the reloads issued past the slice (never read) land before the exit
 
-  // Lane holds token 32v + r and weight rows 32u + 8g + 4h + {0..3} of register group g.
-  float* mine = red + wave * kSkM * kSkPad;
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(mine + (32 * v + r) * kSkPad + 32 * u + 8 * g + 4 * h) =
-            make_float4(acc[u][v][4 * g], acc[u][v][4 * g + 1], acc[u][v][4 * g + 2], acc[u][v][4 * g + 3]);
-  __syncthreads();
-
-  // Thread: token m, columns [c0, c0 + 16) of the tile; wavefront tiles added in order.
-  const int m = tid >> 2, c0 = (tid & 3) * 16;
+  // Lane holds token (lane & 31) of token half (wave >> 1) and weight rows
+  // 8g + 4(lane >> 5) + {0..3} of weight half (wave & 1), g = 0..3.
+  const int64_t m = tr;
   if (m >= a.M) return;
-  float o[16];
 #pragma unroll
-  for (int q = 0; q < 16; q += 4) {
-    float4 acc4 = *reinterpret_cast<const float4*>(red + m * kSkPad + c0 + q);
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const float4 x = *reinterpret_cast<const float4*>(red + w * kSkM * kSkPad + m * kSkPad + c0 + q);
-      acc4.x += x.x;
-      acc4.y += x.y;
-      acc4.z += x.z;
-      acc4.w += x.w;
+  for (int g = 0; g < 4; ++g) {
+    const int64_t col = n0 + 32 * (wave & 1) + 8 * g + 4 * half;
+    if (col >= a.N) continue;
+    if (a.S == 1) {
+      const uint32_t lo = f32_to_bf16_bits(acc[4 * g]) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[4 * g + 1])) << 16);
+      const uint32_t hi = f32_to_bf16_bits(acc[4 * g + 2]) | (static_cast<uint32_t>(f32_to_bf16_bits(acc[4 * g + 3])) << 16);
+      *reinterpret_cast<uint2*>(a.C + m * a.ldc + col) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(a.partials + (static_cast<int64_t>(sp) * a.M + m) * a.N + col) =
+          make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
     }
-    o[q] = acc4.x;
-    o[q + 1] = acc4.y;
-    o[q + 2] = acc4.z;
-    o[q + 3] = acc4.w;
-  }
-  const int64_t col = n0 + c0;
-  if (col >= a.N) return;  // N is a multiple of 64: whole 16-column groups are in or out
-  if (a.S == 1) {
-    uint32_t pk[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      pk[q] = f32_to_bf16_bits(o[2 * q]) | (static_cast<uint32_t>(f32_to_bf16_bits(o[2 * q + 1])) << 16);
-    u32x4* dst = reinterpret_cast<u32x4*>(a.C + m * a.ldc + col);
-    dst[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    dst[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-  } else {
-    float4* dst = reinterpret_cast<float4*>(a.partials + (static_cast<int64_t>(sp) * a.M + m) * a.N + col);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
   }
 }
 
 // C = bf16(sum over planes s = 0..S-1 of partials[s]), planes added in order. Four columns per
-// thread.
-__global__ __launch_bounds__(256) void skinny_finish_kernel(const float* __restrict__ partials, int S, int64_t M,
+// thread; the S loads are issued together (S known at compile time), so the pass costs one
+// memory round trip.
+template <int S>
+__global__ __launch_bounds__(256) void skinny_finish_kernel(const float* __restrict__ partials, int64_t M,
                                                             int64_t N, uint16_t* __restrict__ C, int64_t ldc) {
   const int64_t i4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t plane4 = M * N / 4;
   if (i4 >= plane4) return;
   const float4* p = reinterpret_cast<const float4*>(partials);
-  float4 acc = p[i4];
+  float4 x[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) x[s] = p[s * plane4 + i4];
+  float4 acc = x[0];
+#pragma unroll
   for (int s = 1; s < S; ++s) {
-    const float4 x = p[s * plane4 + i4];
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
+    acc.x += x[s].x;
+    acc.y += x[s].y;
+    acc.z += x[s].z;
+    acc.w += x[s].w;
   }
   const int64_t m = (i4 * 4) / N, n = (i4 * 4) % N;
   const uint32_t lo = f32_to_bf16_bits(acc.x) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y)) << 16);
@@ -183,8 +189,8 @@ int gemm_skinny_splits(int64_t N, int64_t K) {
   const int64_t tiles = (N + kSkN - 1) / kSkN;
   const int64_t nk = K / 64;
   int s = 1;
-  // about 128 workgroups, each wavefront keeping at least one 64-k block
-  while (s * 2 <= kSkMaxSplit && tiles * s < 128 && s * 2 * 4 <= nk) s *= 2;
+  // about 256 workgroups (one per CU), each k-slice keeping at least one 64-k stage
+  while (s * 2 <= kSkMaxSplit && tiles * s < 256 && s * 2 <= nk) s *= 2;
   return s;
 }
 
@@ -216,8 +222,14 @@ hipError_t launch_gemm_skinny(const GemmCall& c, float* partials, size_t partial
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.S == 1) return e;
   const int64_t n4 = a.M * a.N / 4;
-  hipLaunchKernelGGL(skinny_finish_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
-                     a.partials, a.S, a.M, a.N, a.C, a.ldc);
+  const dim3 fg(static_cast<unsigned>((n4 + 255) / 256));
+  switch (a.S) {  // a power of two up to kSkMaxSplit
+    case 2: hipLaunchKernelGGL(skinny_finish_kernel<2>, fg, dim3(256), 0, s, a.partials, a.M, a.N, a.C, a.ldc); break;
+    case 4: hipLaunchKernelGGL(skinny_finish_kernel<4>, fg, dim3(256), 0, s, a.partials, a.M, a.N, a.C, a.ldc); break;
+    case 8: hipLaunchKernelGGL(skinny_finish_kernel<8>, fg, dim3(256), 0, s, a.partials, a.M, a.N, a.C, a.ldc); break;
+    case 16: hipLaunchKernelGGL(skinny_finish_kernel<16>, fg, dim3(256), 0, s, a.partials, a.M, a.N, a.C, a.ldc); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
