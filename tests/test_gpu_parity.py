@@ -343,6 +343,11 @@ def test_latent_projections_few_tokens(T):
 
 # --------------------------------------------------------------------------- whole layer
 
+# A few experts take most of 24576 assignments (Zipf score bias): experts of 16 or more 256-row
+# tiles hold most of the main tile list, so the GEMMs deal its tiles to the XCDs one by one
+# (the spread order); test_spread_case_uses_spread_order checks that the case does.
+SPREAD_CASE = ("skewed", 12288, dict(d_model=256, num_experts=16, top_k=2, hidden_size=128))
+
 LAYER_CASES = [
     ("tiny_f32", None, {}),
     ("tiny_f32", 37, dict(num_experts=8, top_k=8)),                       # k = E
@@ -357,6 +362,7 @@ LAYER_CASES = [
                             up_proj_input_norm=False)),
     ("olmoe", 200, dict(d_model=256, num_experts=12, top_k=3, hidden_size=128, gating_function="topk_softmax",
                         restore_weight_scale=True, router_bias=True)),
+    SPREAD_CASE,
 ]
 
 
@@ -387,6 +393,20 @@ def run_layer_case(name, T, over):
 def test_layer_parity(case):
     banner(f"layer {case}")
     run_layer_case(*case)
+
+
+def test_spread_case_uses_spread_order():
+    """The rule the dispatch applies to a main tile list (most of its 256-row tiles in experts
+    of at least 16 such tiles; a remainder above 128 rows takes one more tile), evaluated on
+    the GPU's own expert counts for the spread case."""
+    name, T, over = SPREAD_CASE
+    cfg, w, x = workloads.make_workload(name, tokens=T, **over)
+    layer = moe.MoELayer(cfg, to_device_weights(w))
+    _, r = layer(x.cuda(), routing=True)
+    counts = r["batch_size_per_expert"].cpu().numpy().astype(np.int64)
+    tiles = counts // 256 + (counts % 256 > 128)
+    large = tiles[tiles >= 16].sum()
+    assert tiles.sum() > 0 and 2 * large >= tiles.sum(), (counts, tiles)
 
 
 def test_layer_deterministic():

@@ -220,11 +220,11 @@ WsLayout ws_layout(const Layer& ly) {
   w.perm = c.take(A * 4);
   w.inv = c.take(A * 4);
   w.scratch = c.take(dispatch_scratch_bytes(ly));
-  w.tcount = c.take(4);
+  w.tcount = c.take(8);
   w.texpert = c.take(static_cast<size_t>(w.tile_cap) * 4);
   w.trow0 = c.take(static_cast<size_t>(w.tile_cap) * 4);
   w.trows = c.take(static_cast<size_t>(w.tile_cap) * 4);
-  w.scount = c.take(4);
+  w.scount = c.take(8);
   w.sexpert = c.take(static_cast<size_t>(w.small_cap) * 4);
   w.srow0 = c.take(static_cast<size_t>(w.small_cap) * 4);
   w.srows = c.take(static_cast<size_t>(w.small_cap) * 4);
@@ -469,11 +469,11 @@ BwdLayout bwd_layout(const Layer& ly) {
   const TilePlan plan = tile_plan(ly);
   b.tile_cap = static_cast<int32_t>((A + plan.bm - 1) / plan.bm + E);
   b.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs)) : 0;
-  b.tcount = c.take(4);
+  b.tcount = c.take(8);
   b.texpert = c.take(static_cast<size_t>(b.tile_cap) * 4);
   b.trow0 = c.take(static_cast<size_t>(b.tile_cap) * 4);
   b.trows = c.take(static_cast<size_t>(b.tile_cap) * 4);
-  b.scount = c.take(4);
+  b.scount = c.take(8);
   b.sexpert = c.take(static_cast<size_t>(b.small_cap) * 4);
   b.srow0 = c.take(static_cast<size_t>(b.small_cap) * 4);
   b.srows = c.take(static_cast<size_t>(b.small_cap) * 4);

@@ -149,12 +149,17 @@ struct Layer {
 
 // Per-expert M-tile list consumed by the grouped GEMMs (device memory, built on the device).
 struct TileList {
-  int32_t* count;   // [1]   number of M-tiles
+  int32_t* count;   // [2]   number of M-tiles; [1]: spread tile order (see kSpreadMinMTiles)
   int32_t* expert;  // [cap] expert of each M-tile
   int32_t* row0;    // [cap] first sorted row of each M-tile
   int32_t* rows;    // [cap] valid rows (<= BM)
   int32_t cap;
 };
+
+// A main tile list whose M-tiles mostly belong to experts of at least this many M-tiles is
+// marked (count[1] = 1) for the GEMMs' spread tile order across the XCDs; remainder lists
+// never are.
+constexpr int kSpreadMinMTiles = 16;
 
 // How an expert's rows are cut into M-tiles: full tiles of bm rows; the remainder r = rows % bm
 // goes to one more tile of that list when r > small_max, else to ceil(r / bs) tiles of bs rows

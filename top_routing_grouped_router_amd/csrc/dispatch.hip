@@ -210,10 +210,18 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
   const int ts = block_inclusive_scan(ns, sh) - ns;
   __syncthreads();
   const int total_s = sh[16];
+  __syncthreads();
+  block_inclusive_scan(nb >= kSpreadMinMTiles ? nb : 0, sh);  // M-tiles of large experts
+  __syncthreads();
+  const int in_large = sh[16];
   if (e < E) write_expert_tiles(e, excl, c, plan, nb, ns, tb, ts, tiles, small_tiles);
   if (threadIdx.x == 0) {
-    *tiles.count = min(total, tiles.cap);
-    if (small_tiles.cap > 0) *small_tiles.count = min(total_s, small_tiles.cap);
+    tiles.count[0] = min(total, tiles.cap);
+    tiles.count[1] = total > 0 && 2 * in_large >= total ? 1 : 0;
+    if (small_tiles.cap > 0) {
+      small_tiles.count[0] = min(total_s, small_tiles.cap);
+      small_tiles.count[1] = 0;
+    }
   }
 }
 
@@ -360,11 +368,20 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     __syncthreads();
     block_exclusive_scan_e(ms, E, ts, sh);
     __syncthreads();
-    for (int e = tid; e < E; e += 256)
+    if (tid == 0) sh[16] = 0;
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
       write_expert_tiles(e, off[e], off[e + 1] - off[e], plan, mt[e], ms[e], tb[e], ts[e], tiles, small_tiles);
+      if (mt[e] >= kSpreadMinMTiles) atomicAdd(&sh[16], mt[e]);  // M-tiles of large experts
+    }
+    __syncthreads();
     if (tid == 0) {
-      *tiles.count = min(tb[E], tiles.cap);
-      if (small_tiles.cap > 0) *small_tiles.count = min(ts[E], small_tiles.cap);
+      tiles.count[0] = min(tb[E], tiles.cap);
+      tiles.count[1] = tb[E] > 0 && 2 * sh[16] >= tb[E] ? 1 : 0;
+      if (small_tiles.cap > 0) {
+        small_tiles.count[0] = min(ts[E], small_tiles.cap);
+        small_tiles.count[1] = 0;
+      }
     }
     __syncthreads();
   }

@@ -23,10 +23,12 @@
 //     permuted copy of the tokens is never materialised; the GEMM2 epilogue scatters rows to
 //     assignment order, so the combine reads each token's k rows contiguously.
 //   * Persistent grid (one workgroup per CU slot). Workgroup i runs on XCD i % 8; the linear
-//     tile sequence is cut into 8 contiguous chunks, one per XCD, and inside a chunk tiles go
-//     in groups of 4 M-tiles x all N-tiles, so the tiles an XCD runs together share A and B
-//     panels in that XCD's L2. Small tiles use only as many workgroups of an XCD as finish its
-//     chunk in the same number of rounds, so no round runs part-empty.
+//     tile sequence goes in groups of 4 M-tiles x all N-tiles and is cut into 8 contiguous
+//     chunks, one per XCD, so the tiles an XCD runs together share A and B panels in that
+//     XCD's L2. Tile lists dominated by experts of 16 or more M-tiles are instead dealt to the
+//     XCDs tile by tile, so the XCDs run neighbouring groups of one expert together and share
+//     panels through the last-level cache as well. Small tiles use only as many workgroups of
+//     an XCD as finish its chunk in the same number of rounds, so no round runs part-empty.
 //   * Operands reach LDS by DMA (16 bytes per lane, no register round trip); each 64-k stage
 //     is one whole 128-byte line per staged row. Row-major operands use buffer_load ... lds
 //     through a buffer descriptor per operand, the k-stage step a scalar offset; measured on
@@ -313,9 +315,20 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   const int64_t total = total_m * ntn;
   const int xcd = blockIdx.x % kXcds;
   const int64_t chunk = (total + kXcds - 1) / kXcds;
+  // Tiles go in groups of kGroupM M-tiles x all N-tiles (consecutive in the linear sequence),
+  // and each XCD runs about 32 of them at a time: kGroupM M-tiles x 8 N-tiles, whose operand
+  // panels share that XCD's L2. Spread order: XCD x takes tiles x, x + 8, x + 16, ... of the
+  // sequence, so the eight XCDs run sixteen neighbouring M-tiles x all N-tiles at once, each
+  // XCD still kGroupM M-tiles x half the N-tiles; every token panel is then shared by two XCDs
+  // and every weight panel by four through the last-level cache. That pays where an expert
+  // spans those sixteen M-tiles; with smaller experts an XCD's window would straddle several
+  // experts, so there (and for dense products, where it measured no better) each XCD takes one
+  // contiguous eighth of the sequence. The dispatch marks a main tile list (count[1]) when most
+  // of its M-tiles belong to experts of at least kSpreadMinMTiles M-tiles.
+  const bool spread = !WGRAD && c.dense_M <= 0 && c.tiles.count[1] != 0;
   // Small tiles stream weights from HBM, and a last round that only part of the workgroups
   // run leaves bandwidth unused: there only as many workgroups of the XCD take part as still
-  // finish its chunk in the same number of rounds, each taking the same number of tiles.
+  // finish its slots in the same number of rounds, each taking the same number of tiles.
   // (Large tiles are bound by the matrix cores, where the slowest workgroup's tile count
   // decides either way.)
   int per_xcd = gridDim.x / kXcds;
@@ -361,7 +374,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     int32_t scsrc;       // MXFP8 scale loads of token rows: source row
   };
 
-  // it: the tile's slot in this XCD's chunk, or (weight-gradient mode) its index in the
+  // it: the tile's position in the linear sequence, or (weight-gradient mode) its index in the
   // heavy-first sequence handed out by the tile counter
   auto fetch = [&](int64_t it, TileFetch& f) {
     int64_t mt;
@@ -375,8 +388,7 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       mt = g * wg_mtiles + local / ntn;
       f.nt = local % ntn;
     } else {
-      const int64_t lin = xcd * chunk + it;
-      // tiles go in groups of kGroupM M-tiles x all N-tiles
+      const int64_t lin = it;
       const int64_t gsz = kGroupM * ntn;
       const int64_t grp_i = lin / gsz, first_m = grp_i * kGroupM;
       const int64_t gm = min(static_cast<int64_t>(kGroupM), total_m - first_m);
@@ -903,8 +915,17 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     if (tid == 0) s_sched[0] = atomicAdd(c.tile_counter, 1);
     __syncthreads();
   }
-  int64_t it = WGRAD ? static_cast<int64_t>(sched[0]) : blockIdx.x / kXcds;
-  if (WGRAD ? it >= total : (it >= chunk || it >= per_xcd || xcd * chunk + it >= total)) return;
+  // The tile loop is compiled once per tile order (SP: spread), so neither copy keeps the
+  // other's bounds live (they share the kernel's registers, and the large tiles have none to
+  // spare). Other modes: it is the tile's position in the linear sequence; this workgroup's
+  // tiles are those from its first in steps of it_step below lin_end.
+  auto tile_loop = [&](auto sp_c) __attribute__((always_inline)) {
+  constexpr bool SP = decltype(sp_c)::value;
+  const int64_t slot = blockIdx.x / kXcds;
+  const int64_t lin_end = SP ? total : min(total, (xcd + 1) * chunk);
+  const int64_t it_step = (SP ? kXcds : 1) * static_cast<int64_t>(per_xcd);
+  int64_t it = WGRAD ? static_cast<int64_t>(sched[0]) : (SP ? xcd + slot * kXcds : xcd * chunk + slot);
+  if (WGRAD ? it >= total : (slot >= per_xcd || it >= lin_end)) return;
   int parity = 1;
   TileFetch fnext;
   TileState cur;
@@ -921,8 +942,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     if (WGRAD && tid == 0) sched[parity] = atomicAdd(c.tile_counter, 1);
     const int nk = WGRAD ? cur.nk : static_cast<int>(c.Kd / S::BK);
     // EARLY: the next tile of this workgroup's sequence, fetched during the first stage
-    const int64_t it_pre = it + per_xcd;
-    const bool fetch_next = EARLY && it_pre < chunk && xcd * chunk + it_pre < total;
+    const int64_t it_pre = it + it_step;
+    const bool fetch_next = EARLY && it_pre < lin_end;
     if (fetch_next && nk <= 0) fetch(it_pre, fnext);
     // The MFMA work of k-stage kt from slot `la`, with its scheduling directives. late
     // (staggered loads, see the k-loop below): this wavefront's loads of the stage come after
@@ -1034,8 +1055,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       more = it_next < total;
       parity ^= 1;
     } else {
-      it_next = it + per_xcd;
-      more = it_next < chunk && xcd * chunk + it_next < total;
+      it_next = it + it_step;
+      more = it_next < lin_end;
     }
     TileState nxt;
     epilogue(cur, more, fnext, it_next, nxt);
@@ -1043,6 +1064,11 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     cur = nxt;
     it = it_next;
   }
+  };
+  if (spread)
+    tile_loop(std::true_type{});
+  else
+    tile_loop(std::false_type{});
   // Nothing is left in flight that writes LDS (each tile's last stage issues no refill and the
   // last tile issues no next stage), but keep the invariant explicit before LDS is released.
   wait_vmcnt<0>();
