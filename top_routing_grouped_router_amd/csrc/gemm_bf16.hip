@@ -274,13 +274,13 @@ __device__ __forceinline__ unsigned char* scale_area() {
   }
 }
 
-// TRANS: bit 0 = the token operand A is contraction-major, bit 1 = the weight operand B is (see
-// GemmCall::trans). WGRAD: weight-gradient mode, the contraction runs over each group's rows
-// (GemmCall::group_offsets). SWIGLU_BWD: the SwiGLU-backward epilogue (GemmCall::bwd_h).
-// H_OUT: the SwiGLU epilogue also stores the pre-activation (GemmCall::h_out).
-template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false, bool OUT_MX = false, int TRANS = 0,
-          bool WGRAD = false, bool SWIGLU_BWD = false, bool H_OUT = false>
-__global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
+// The kernel's work, for one tile order (SP: spread, see below); the kernel after it picks one.
+// lds0 / lds1: the two ring slots, separate LDS arrays, so the compiler can tell that DMA loads
+// into one slot never touch another: it then does not hold the epilogue's staging in slot 1
+// until the next tile's loads into slot 0 have landed.
+template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32, bool OUT_MX, int TRANS, bool WGRAD,
+          bool SWIGLU_BWD, bool H_OUT, bool SP>
+__device__ __forceinline__ void gemm_bf16_body(const GemmCall& c, unsigned char* lds0, unsigned char* lds1) {
   static_assert(S::NSTAGE == 2, "the persistent loop runs a two-slot ring");
   constexpr bool TA = (TRANS & 1) != 0, TB = (TRANS & 2) != 0;
   static_assert(!(TA || TB) || (!S::MX && S::PLANES == 1 && S::BK == 64 && !SWIGLU && !OUT_F32 && !OUT_MX),
@@ -293,11 +293,6 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   static_assert(!SWIGLU || S::TN % 2 == 0, "SwiGLU pairs up/gate sub-tiles inside a wavefront");
   static_assert(!SWIGLU || S::PLANES == 1, "planes are for plain products");
   using OutT = typename std::conditional<OUT_F32, float, uint16_t>::type;
-  // The two ring slots (and the MXFP8 scale groups) are separate LDS arrays, so the compiler
-  // can tell that DMA loads into one slot never touch another: it then does not hold the
-  // epilogue's staging in slot 1 until the next tile's loads into slot 0 have landed.
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[S::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[S::STAGE];
   unsigned char* const ldssc = scale_area<S>();
   const int tid = threadIdx.x, lane = tid & 63;
   // wavefront coordinates are uniform per wavefront: keep them in scalar registers
@@ -324,8 +319,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   // spans those sixteen M-tiles; with smaller experts an XCD's window would straddle several
   // experts, so there (and for dense products, where it measured no better) each XCD takes one
   // contiguous eighth of the sequence. The dispatch marks a main tile list (count[1]) when most
-  // of its M-tiles belong to experts of at least kSpreadMinMTiles M-tiles.
-  const bool spread = !WGRAD && c.dense_M <= 0 && c.tiles.count[1] != 0;
+  // of its M-tiles belong to experts of at least kSpreadMinMTiles M-tiles; the kernel then runs
+  // the SP copy of this body.
   // Small tiles stream weights from HBM, and a last round that only part of the workgroups
   // run leaves bandwidth unused: there only as many workgroups of the XCD take part as still
   // finish its slots in the same number of rounds, each taking the same number of tiles.
@@ -915,12 +910,8 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     if (tid == 0) s_sched[0] = atomicAdd(c.tile_counter, 1);
     __syncthreads();
   }
-  // The tile loop is compiled once per tile order (SP: spread), so neither copy keeps the
-  // other's bounds live (they share the kernel's registers, and the large tiles have none to
-  // spare). Other modes: it is the tile's position in the linear sequence; this workgroup's
-  // tiles are those from its first in steps of it_step below lin_end.
-  auto tile_loop = [&](auto sp_c) __attribute__((always_inline)) {
-  constexpr bool SP = decltype(sp_c)::value;
+  // Other modes: it is the tile's position in the linear sequence; this workgroup's tiles are
+  // those from its first in steps of it_step below lin_end.
   const int64_t slot = blockIdx.x / kXcds;
   const int64_t lin_end = SP ? total : min(total, (xcd + 1) * chunk);
   const int64_t it_step = (SP ? kXcds : 1) * static_cast<int64_t>(per_xcd);
@@ -1064,14 +1055,32 @@ __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     cur = nxt;
     it = it_next;
   }
-  };
-  if (spread)
-    tile_loop(std::true_type{});
-  else
-    tile_loop(std::false_type{});
   // Nothing is left in flight that writes LDS (each tile's last stage issues no refill and the
   // last tile issues no next stage), but keep the invariant explicit before LDS is released.
   wait_vmcnt<0>();
+}
+
+// TRANS: bit 0 = the token operand A is contraction-major, bit 1 = the weight operand B is (see
+// GemmCall::trans). WGRAD: weight-gradient mode, the contraction runs over each group's rows
+// (GemmCall::group_offsets). SWIGLU_BWD: the SwiGLU-backward epilogue (GemmCall::bwd_h).
+// H_OUT: the SwiGLU epilogue also stores the pre-activation (GemmCall::h_out).
+// Forward row-major products over a marked tile list run the spread tile order. The body is
+// compiled once per order, so neither copy keeps the other's loop bounds live (the large tiles
+// have no registers to spare); the backward's contraction-major kernels have one copy (a second
+// cost them registers and time).
+template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false, bool OUT_MX = false, int TRANS = 0,
+          bool WGRAD = false, bool SWIGLU_BWD = false, bool H_OUT = false>
+__global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[S::STAGE];
+  constexpr bool kSpreadable = !WGRAD && TRANS == 0;
+  if constexpr (kSpreadable) {
+    if (c.dense_M <= 0 && c.tiles.count[1] != 0) {
+      gemm_bf16_body<S, SWIGLU, GATHER, SCATTER, OUT_F32, OUT_MX, TRANS, WGRAD, SWIGLU_BWD, H_OUT, true>(c, lds0, lds1);
+      return;
+    }
+  }
+  gemm_bf16_body<S, SWIGLU, GATHER, SCATTER, OUT_F32, OUT_MX, TRANS, WGRAD, SWIGLU_BWD, H_OUT, false>(c, lds0, lds1);
 }
 
 template <class S>
