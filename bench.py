@@ -93,12 +93,38 @@ STAGE_SOURCES = {
 }
 
 
+def _code_only(text):
+    """The source with comments and blank space removed (string literals kept as written), so
+    that a comment-only edit leaves the hash of the code unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch == '"' or ch == "'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_sha256(names):
+    """Hash of the code (comments and layout aside) of the sources a stage's kernels build from:
+    a traffic record applies while it matches."""
     h = hashlib.sha256()
     for name in names:
         h.update(name.encode())
-        with open(os.path.join(CSRC, name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -323,7 +323,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmCall& c, unsigned char*
   // the SP copy of this body.
   // Small tiles stream weights from HBM, and a last round that only part of the workgroups
   // run leaves bandwidth unused: there only as many workgroups of the XCD take part as still
-  // finish its slots in the same number of rounds, each taking the same number of tiles.
+  // finish its share of the tiles in the same number of rounds, each taking the same number.
   // (Large tiles are bound by the matrix cores, where the slowest workgroup's tile count
   // decides either way.)
   int per_xcd = gridDim.x / kXcds;
