@@ -1065,16 +1065,15 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmCall& c, unsigned char*
 // GemmCall::trans). WGRAD: weight-gradient mode, the contraction runs over each group's rows
 // (GemmCall::group_offsets). SWIGLU_BWD: the SwiGLU-backward epilogue (GemmCall::bwd_h).
 // H_OUT: the SwiGLU epilogue also stores the pre-activation (GemmCall::h_out).
-// Forward row-major products over a marked tile list run the spread tile order. The body is
-// compiled once per order, so neither copy keeps the other's loop bounds live (the large tiles
-// have no registers to spare); the backward's contraction-major kernels have one copy (a second
-// cost them registers and time).
+// Grouped products over a marked tile list run the spread tile order. The body is compiled once
+// per order, so neither copy keeps the other's loop bounds live (the large tiles have no
+// registers to spare); weight-gradient kernels, whose tiles are handed out, have one copy.
 template <class S, bool SWIGLU, bool GATHER, bool SCATTER, bool OUT_F32 = false, bool OUT_MX = false, int TRANS = 0,
           bool WGRAD = false, bool SWIGLU_BWD = false, bool H_OUT = false>
 __global__ __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_bf16_kernel(GemmCall c) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[S::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[S::STAGE];
-  constexpr bool kSpreadable = !WGRAD && TRANS == 0;
+  constexpr bool kSpreadable = !WGRAD;
   if constexpr (kSpreadable) {
     if (c.dense_M <= 0 && c.tiles.count[1] != 0) {
       gemm_bf16_body<S, SWIGLU, GATHER, SCATTER, OUT_F32, OUT_MX, TRANS, WGRAD, SWIGLU_BWD, H_OUT, true>(c, lds0, lds1);
