@@ -34,10 +34,10 @@
 //     through a buffer descriptor per operand, the k-stage step a scalar offset; measured on
 //     the same box, that streams faster than global_load_lds (a 32768 x 4096 x 4096 dense
 //     product 1191 -> 1248 TFLOP/s), and the operand loads need no per-lane 64-bit addresses.
-//   * Staggered load issue (large tiles of the forward and of the input gradients): of the two
-//     wavefronts sharing a SIMD, one issues its share of the next stage's loads before its first
-//     fragment reads, the other after its first k16 step, so the pair does not stall together
-//     on a full address queue.
+//   * Staggered load issue (large tiles, weight-gradient tiles): of the two wavefronts sharing a
+//     SIMD, one issues its share of the next stage's loads before its first fragment reads, the
+//     other after its first k16 step, so the pair does not stall together on a full address
+//     queue.
 //   * Epilogue through LDS: the accumulators leave the MFMA layout as 8-byte pieces of 32
 //     different rows, so stored directly every instruction writes 32 partial lines. They are
 //     staged in the free ring slot instead and stored as whole rows (full 128-byte lines per
@@ -681,10 +681,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmCall& c, unsigned char*
   // wavefront issues exactly NQ operand loads (plus one scale load for MXFP8 wavefronts below
   // NSC), the count the scatter wait below relies on. Other shapes issue it in the last round.
   constexpr bool EARLY = !WGRAD && !S::MX && S::BM == 256 && S::NI % S::NW == 0;
-  // Large tiles stagger their loads (see the k-loop): every k-stage issues its loads, the last
-  // one of a tile reloading its own stage into the free slot, so the epilogue first waits for
-  // those before it reuses a slot.
-  constexpr bool STAGGER = EARLY;
+  // Large tiles (and the weight-gradient tiles) stagger their loads (see the k-loop): every
+  // k-stage issues its loads, the last one of a tile reloading its own stage into the free slot,
+  // so the epilogue first waits for those before it reuses a slot.
+  constexpr bool STAGGER = EARLY || WGRAD;
   constexpr int NSIDX = SCATTER ? (EARLY ? NR * KI : KI) : 1;
   auto epilogue = [&](const TileState& t, bool more, const TileFetch& fn, int64_t it_next, TileState& nx) {
     // The thread index passes through an empty asm statement: the epilogue's per-lane addresses
