@@ -298,7 +298,9 @@ __device__ void block_exclusive_scan_e(const int32_t* v, int E, int32_t* out, in
 // histogram, offsets, M-tile list and stable permutation, with no intermediate global
 // buffers. Pass 1 counts with LDS atomics (exact); pass 2 walks the tokens in chunks of 256
 // in order and ranks each copy like rank_kernel (64-bit per-wavefront masks), on top of the
-// running count of its expert from the earlier chunks.
+// running count of its expert from the earlier chunks. The first 256 tokens' entries are read
+// from memory once for both passes, and each pair of per-expert counts is scanned as one packed
+// value.
 constexpr int kSmallTokens = 1024;
 constexpr int kMaxTopK = MOE_MAX_TOP_K;  // entries per token (top_k is validated against it)
 
@@ -322,19 +324,26 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   __shared__ int sh[17];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t A = T * k;
+  // Two counts packed in one scan (16 bits each): A <= kSmallTokens * kMaxTopK assignments.
+  static_assert(kSmallTokens * kMaxTopK < 65536, "packed scans");
 
+  // Each token's k entries are read as independent loads; those of the first 256 tokens (all of
+  // a decode-sized batch) stay in registers for the second pass. The zeroing below overlaps the
+  // first chunk's loads.
+  int ek0[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) ek0[j] = (tid < T && j < k) ? idx[static_cast<int64_t>(tid) * k + j] : -1;
   for (int e = tid; e < E; e += 256) run[e] = 0;
   __syncthreads();
-  // Each token's k entries are read once, as independent loads, and kept in registers; an
-  // entry repeating an earlier expert of its token is not counted.
+  // An entry repeating an earlier expert of its token is not counted.
   for (int64_t t = tid; t < T; t += 256) {
     int ek[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) ek[j] = j < k ? idx[t * k + j] : -1;
+    for (int j = 0; j < kMaxTopK; ++j) ek[j] = t < 256 ? ek0[j] : (j < k ? idx[t * k + j] : -1);
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       const int e = ek[j];
-      if (j >= k || e < 0 || e >= E) continue;
+      if (e < 0 || e >= E) continue;
       bool repeat = false;
 #pragma unroll
       for (int q = 0; q < j; ++q) repeat |= ek[q] == e;
@@ -342,14 +351,19 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     }
   }
   __syncthreads();
+  // kept | dropped << 16, scanned once
   for (int e = tid; e < E; e += 256) {
-    kc[e] = capacity > 0 ? min(run[e], capacity) : run[e];
-    dc[e] = run[e] - kc[e];
+    const int kept = capacity > 0 ? min(run[e], capacity) : run[e];
+    kc[e] = kept | ((run[e] - kept) << 16);
   }
   __syncthreads();
   block_exclusive_scan_e(kc, E, off, sh);
   __syncthreads();
-  block_exclusive_scan_e(dc, E, doff, sh);
+  for (int e = tid; e <= E; e += 256) {
+    const int v = off[e];
+    off[e] = v & 0xFFFF;
+    doff[e] = v >> 16;
+  }
   __syncthreads();
   // positions past the kept and dropped assignments belong to no entry
   for (int64_t p = static_cast<int64_t>(off[E]) + doff[E] + tid; p < A; p += 256) perm[p] = -1;
@@ -360,15 +374,21 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     expert_tile_counts(off[e + 1] - off[e], plan, nb, ns);
     mt[e] = nb;
     ms[e] = ns;
+    dc[e] = nb | (ns << 16);
   }
   if (tid == 0) offsets[E] = off[E];
   __syncthreads();
   if (tiles.cap > 0) {
-    block_exclusive_scan_e(mt, E, tb, sh);
-    __syncthreads();
-    block_exclusive_scan_e(ms, E, ts, sh);
+    // first tile of each list, scanned once (packed as above); tb[E] overwrites dc[0] only
+    // after every thread has read its entries of dc
+    block_exclusive_scan_e(dc, E, tb, sh);
     __syncthreads();
     if (tid == 0) sh[16] = 0;
+    for (int e = tid; e <= E; e += 256) {
+      const int v = tb[e];
+      tb[e] = v & 0xFFFF;
+      ts[e] = v >> 16;
+    }
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
       write_expert_tiles(e, off[e], off[e + 1] - off[e], plan, mt[e], ms[e], tb[e], ts[e], tiles, small_tiles);
@@ -390,29 +410,28 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
 
   const uint64_t below = (1ull << lane) - 1ull;
   for (int64_t t0 = 0; t0 < T; t0 += 256) {
-    for (int i = tid; i < 4 * E; i += 256) bits[i] = 0;
+    // only the wavefronts holding tokens of this chunk keep masks
+    const int nwa = static_cast<int>(min(static_cast<int64_t>(4), (T - t0 + 63) / 64));
+    for (int i = tid; i < nwa * E; i += 256) bits[i] = 0;
     __syncthreads();
     const int64_t t = t0 + tid;
     uint32_t rep = 0;  // bit j: entry j repeats an earlier expert of the token
-    int ek[kMaxTopK];  // the token's entries, read once
+    int ek[kMaxTopK];  // the token's entries
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) ek[j] = (t < T && j < k) ? idx[t * k + j] : -1;
-    if (t < T) {
+    for (int j = 0; j < kMaxTopK; ++j) ek[j] = t0 == 0 ? ek0[j] : ((t < T && j < k) ? idx[t * k + j] : -1);
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        const int e = ek[j];
-        if (j < k && e >= 0 && e < E) {
-          const unsigned long long old =
-              atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]), 1ull << lane);
-          if (old & (1ull << lane)) rep |= 1u << j;
-        }
+    for (int j = 0; j < kMaxTopK; ++j) {
+      const int e = ek[j];
+      if (e >= 0 && e < E) {
+        const unsigned long long old =
+            atomicOr(reinterpret_cast<unsigned long long*>(&bits[wave * E + e]), 1ull << lane);
+        if (old & (1ull << lane)) rep |= 1u << j;
       }
     }
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
       int r = run[e];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < nwa; ++w) {
         pre[w * E + e] = r;
         r += __popcll(bits[w * E + e]);
       }
