@@ -96,15 +96,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyArgs a) {
 #endif
   // stage s of the slice into ring slot s % kSkSlots (stages past the slice reload its last one)
   auto issue = [&](int s) {
+#if defined(__HIP_DEVICE_COMPILE__)
     const int sc = min(s, ns - 1);
     unsigned char* st = ring + (s % kSkSlots) * kSkStage;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#if defined(__HIP_DEVICE_COMPILE__)
+    for (int q = 0; q < 4; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a[q] ? ra : rb, SK_LDS(st + (wave + 4 * q) * 1024), 16, off[q],
                                                static_cast<uint32_t>(sc) * 128, 0, 0);
+#else
+    (void)s;
 #endif
-    }
   };
 
   f32x16 acc;
