@@ -257,6 +257,47 @@ def test_experts_forward(case):
     assert_close(np32(y), ref_assign, cfg["dtype"], "expert outputs", flips)
 
 
+# Expert row counts whose main tile list (256-row M-tiles, hidden 128: one up/gate tile per
+# M-tile) is 260 M-tiles: one whole round of a 256-workgroup grid and a last round of 4 tiles,
+# which the dispatch moves to the remainder list (64-row tiles) from one expert -- the one with
+# a remainder already; none has one; none has one and the chosen expert's last M-tile is partial.
+TAIL_COUNTS = [
+    [70 * 256, 70 * 256, 70 * 256, 50 * 256 + 40],
+    [130 * 256, 130 * 256],
+    [70 * 256 + 200, 70 * 256, 70 * 256, 49 * 256],
+]
+
+
+def _tail_move(counts, round_tiles, ntn=1, bm=256, small_max=128):
+    """M-tiles the dispatch's thin-last-round rule moves for these counts (0: none)."""
+    nb = [c // bm + (1 if c % bm > small_max else 0) for c in counts]
+    work = sum(nb) * ntn
+    tail = work % round_tiles
+    return -(-tail // ntn) if work > round_tiles and 0 < tail and 8 * tail <= round_tiles else 0
+
+
+@pytest.mark.parametrize("counts", TAIL_COUNTS, ids=lambda c: f"E{len(c)}-{sum(c)}")
+def test_experts_forward_thin_last_round(counts):
+    """Expert outputs when whole M-tiles of the main list run as remainder tiles instead."""
+    E, T = len(counts), sum(counts)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    m = _tail_move(counts, (cus + 7) // 8 * 8)
+    banner(f"experts thin last round {counts}: {m} M-tiles moved on {cus} CUs")
+    cfg, w, x = workloads.make_workload("olmoe", tokens=T, d_model=256, num_experts=E, top_k=1, hidden_size=128)
+    cfgO = O.MoEConfig.from_dict(cfg)
+    wo = oracle_inputs(w)
+    idx = np.repeat(np.arange(E, dtype=np.int64), counts)[np.random.default_rng(11).permutation(T)].reshape(T, 1)
+    z = np32(x)
+    ex = O.run_experts(cfgO, z, idx, wo["w1"], wo["w2"])
+    assert list(ex["counts"]) == counts
+    y = moe.experts_forward(cfg, to_device_weights(w), x.cuda(),
+                            torch.from_numpy(ex["offsets"].astype(np.int32)).cuda(),
+                            torch.from_numpy(ex["perm"].astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    ref_assign = ex["Y"][ex["inv"]]
+    assert_close(np32(y), ref_assign, cfg["dtype"], "expert outputs", 2.0 * bf16_spacing(ref_assign))
+
+
 @pytest.mark.parametrize("case", [("olmoe", 300, dict(d_model=512, num_experts=16, top_k=4, hidden_size=128)),
                                   ("latent896", 300, dict(d_model=512, latent_dim=256, num_experts=32)),
                                   ("tiny_f32", None, {}),

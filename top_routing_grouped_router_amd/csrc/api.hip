@@ -209,8 +209,11 @@ WsLayout ws_layout(const Layer& ly) {
   const size_t es = elem_size(ly);
   const TilePlan plan = tile_plan(ly);
   w.tile_cap = static_cast<int32_t>((A + plan.bm - 1) / plan.bm + E);
-  // at most ceil(small_max / bs) remainder tiles per expert
-  w.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs)) : 0;
+  // at most ceil(small_max / bs) remainder tiles per expert, plus the M-tiles a thin last round
+  // of the main list may move there
+  w.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs) +
+                                                          tail_small_tiles(plan))
+                                   : 0;
   w.logits = c.take(static_cast<size_t>(router_splits(ly)) * T * E * 4);  // logit partial sums
   w.rscratch = c.take(router_scratch_bytes(ly));                            // router weight planes
   w.idx = c.take(A * 4);
@@ -468,7 +471,9 @@ BwdLayout bwd_layout(const Layer& ly) {
   const size_t es = elem_size(ly);
   const TilePlan plan = tile_plan(ly);
   b.tile_cap = static_cast<int32_t>((A + plan.bm - 1) / plan.bm + E);
-  b.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs)) : 0;
+  b.small_cap = plan.small_max > 0 ? static_cast<int32_t>(E * ((plan.small_max + plan.bs - 1) / plan.bs) +
+                                                          tail_small_tiles(plan))
+                                   : 0;
   b.tcount = c.take(8);
   b.texpert = c.take(static_cast<size_t>(b.tile_cap) * 4);
   b.trow0 = c.take(static_cast<size_t>(b.tile_cap) * 4);

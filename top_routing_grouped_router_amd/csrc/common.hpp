@@ -166,11 +166,27 @@ constexpr int kSpreadMinMTiles = 16;
 // in a second list, run by the smaller tile shape (small_max = 0: one list only). With the
 // large shape's 256-row tiles, an expert of 1 + 4 * 256 rows then adds one 64-row tile to the
 // small list instead of a 256-row tile that is almost all padding.
+// Thin last round: the large tiles' persistent grid runs tail_round workgroups at a time, and
+// each main-list M-tile is tail_ntn tiles of the up/gate GEMM. When the main list would leave
+// a last round of at most tail_round / 8 tiles (after at least one whole round), the fewest
+// whole M-tiles that remove it go to the remainder list instead, all from one expert: one that
+// already has remainder tiles (its weights are streamed by the small tiles anyway) if any
+// expert has enough M-tiles, else the lowest-numbered such expert. Outputs do not change: both
+// tile shapes accumulate every output element over k in the same order. tail_round = 0 (or no
+// remainder list) disables the move.
 struct TilePlan {
   int bm;         // rows per tile of the main list
   int bs;         // rows per tile of the remainder list
   int small_max;  // largest remainder sent to the remainder list (0 = none)
+  int tail_round = 0;  // workgroups per round of the main-list GEMMs (0: no tail move)
+  int tail_ntn = 0;    // tiles per main-list M-tile of the up/gate GEMM
 };
+// Largest tail_round the dispatch honours, and the remainder-list room it then needs beyond
+// ceil(small_max / bs) tiles per expert: at most kTailRoundMax / 8 M-tiles move.
+constexpr int kTailRoundMax = 1024;
+inline int tail_small_tiles(const TilePlan& p) {
+  return p.small_max > 0 ? (kTailRoundMax / 8 + 1) * ((p.bm + p.bs - 1) / p.bs) : 0;
+}
 
 // Grid-wide properties cached per device.
 int device_cu_count();
@@ -271,6 +287,10 @@ struct GemmCall {
 
 // bf16 MFMA GEMM; returns the M-tile height it was instantiated with for the chosen variant.
 int gemm_bf16_tile_m(int variant);
+// Workgroups per round of the main-list (large-tile) persistent grid on the current device, and
+// output columns per tile of its up/gate GEMM (the SwiGLU halves of a 256-row weight tile).
+int gemm_bf16_round_tiles();
+int gemm_bf16_swiglu_tile_cols();
 int gemm_bf16_pick_variant(double mean_rows_per_group);
 hipError_t launch_gemm_bf16(const GemmCall& c, int variant, hipStream_t s);
 // Backward GEMMs (bf16). Input gradients: grouped M-tiles of the given variant's tile height,

@@ -19,8 +19,10 @@
 //   scan_cols       one block per expert: exclusive scan of its row of block counts ->
 //                   per-block bases; total -> counts[e].
 //   offsets_tiles   one block: exclusive scan of counts -> offsets; M-tiles per expert
-//                   (ceil(count / BM)) -> the tile list. Experts with no tokens get no tile,
-//                   so their weights are never read.
+//                   (TilePlan: whole tiles, the remainder on one more tile or on the
+//                   remainder list, a thin last round moved there) -> the two tile lists,
+//                   one thread per tile entry. Experts with no tokens get no tile, so their
+//                   weights are never read.
 //   permute         one thread per copy: position = offset + block base + rank.
 //   dispatch_small  all of the above in one workgroup for batches of at most 1024 tokens,
 //                   where four launches would cost more than the work.
@@ -203,6 +205,32 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
   c = c < 0 ? 0 : c;
   int nb = 0, ns = 0;
   if (e < E) expert_tile_counts(c, plan, nb, ns);
+  // Thin last round of the main list (TilePlan): move m whole M-tiles of one expert to the
+  // remainder list. The rule reads only the block-wide total, so every thread agrees on m.
+  block_inclusive_scan(nb, sh);
+  __syncthreads();
+  const int total0 = sh[16];
+  __syncthreads();
+  const int R = plan.tail_round, ntn = plan.tail_ntn;
+  int m = 0;
+  if (small_tiles.cap > 0 && plan.small_max > 0 && R > 0 && R <= kTailRoundMax && ntn > 0) {
+    const int64_t work = static_cast<int64_t>(total0) * ntn;
+    const int tail = static_cast<int>(work % R);
+    if (work > R && tail > 0 && 8 * tail <= R) m = (tail + ntn - 1) / ntn;
+  }
+  if (m > 0) {
+    __shared__ int s_pick;
+    if (threadIdx.x == 0) s_pick = 0x7fffffff;
+    __syncthreads();
+    // experts that already have remainder tiles first, then by index
+    if (e < E && nb >= m) atomicMin(&s_pick, (ns > 0 ? 0 : E) + e);
+    __syncthreads();
+    const int pick = s_pick;
+    if (pick != 0x7fffffff && e == pick % E) {
+      nb -= m;
+      ns = (c - nb * plan.bm + plan.bs - 1) / plan.bs;
+    }
+  }
   const int tb = block_inclusive_scan(nb, sh) - nb;
   __syncthreads();
   const int total = sh[16];
@@ -214,12 +242,46 @@ __global__ __launch_bounds__(1024) void offsets_tiles_kernel(const int32_t* __re
   block_inclusive_scan(nb >= kSpreadMinMTiles ? nb : 0, sh);  // M-tiles of large experts
   __syncthreads();
   const int in_large = sh[16];
-  if (e < E) write_expert_tiles(e, excl, c, plan, nb, ns, tb, ts, tiles, small_tiles);
+  // Tile entries, one thread per tile: tile t of a list belongs to the last expert whose first
+  // tile is at or before t (experts without tiles share their start with the next expert).
+  __shared__ int s_tb[MOE_MAX_EXPERTS], s_ts[MOE_MAX_EXPERTS], s_row[MOE_MAX_EXPERTS], s_cnt[MOE_MAX_EXPERTS],
+      s_srow[MOE_MAX_EXPERTS];
+  if (e < E) {
+    s_tb[e] = tb;
+    s_ts[e] = ts;
+    s_row[e] = excl;
+    s_cnt[e] = c;
+    s_srow[e] = nb * plan.bm;  // first row (inside the expert) of its remainder tiles
+  }
+  __syncthreads();
+  auto owner = [&](const int* start, int t) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  const int nbig = min(total, tiles.cap);
+  for (int t = threadIdx.x; t < nbig; t += blockDim.x) {
+    const int x = owner(s_tb, t), i = t - s_tb[x];
+    tiles.expert[t] = x;
+    tiles.row0[t] = s_row[x] + i * plan.bm;
+    tiles.rows[t] = min(plan.bm, s_cnt[x] - i * plan.bm);
+  }
+  const int nsmall = min(total_s, small_tiles.cap);
+  for (int t = threadIdx.x; t < nsmall; t += blockDim.x) {
+    const int x = owner(s_ts, t), r = s_srow[x] + (t - s_ts[x]) * plan.bs;
+    small_tiles.expert[t] = x;
+    small_tiles.row0[t] = s_row[x] + r;
+    small_tiles.rows[t] = min(plan.bs, s_cnt[x] - r);
+  }
   if (threadIdx.x == 0) {
-    tiles.count[0] = min(total, tiles.cap);
+    tiles.count[0] = nbig;
     tiles.count[1] = total > 0 && 2 * in_large >= total ? 1 : 0;
     if (small_tiles.cap > 0) {
-      small_tiles.count[0] = min(total_s, small_tiles.cap);
+      small_tiles.count[0] = nsmall;
       small_tiles.count[1] = 0;
     }
   }
@@ -467,6 +529,20 @@ size_t dispatch_scratch_bytes(const Layer& ly) {
   return (A + static_cast<size_t>(ly.E) * nblk + static_cast<size_t>(ly.E) + 1) * sizeof(int32_t) + 256;
 }
 
+namespace {
+// The plan with its thin-last-round fields (TilePlan) for the bf16 large tiles of this device.
+// (The one-workgroup dispatch of small batches builds its lists without the move.)
+TilePlan with_tail(const Layer& ly, const TilePlan& plan) {
+  TilePlan p = plan;
+  if (ly.bf16 && !ly.mx && p.small_max > 0) {
+    p.tail_round = gemm_bf16_round_tiles();
+    const int64_t cols = gemm_bf16_swiglu_tile_cols();
+    p.tail_ntn = static_cast<int>((ly.h + cols - 1) / cols);
+  }
+  return p;
+}
+}  // namespace
+
 hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* perm, int32_t* inv, void* scratch, const TileList& tiles,
                            const TileList& small_tiles, const TilePlan& plan, hipStream_t s) {
@@ -491,7 +567,7 @@ hipError_t launch_dispatch(const Layer& ly, const int32_t* idx, int32_t* counts,
                      blk);
   hipLaunchKernelGGL(scan_cols_kernel, dim3(ly.E), dim3(256), 0, s, blk, nblk, counts);
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, counts, nullptr, offsets, ly.E,
-                     plan, tiles, small_tiles, cap, drop_off, perm, A);
+                     with_tail(ly, plan), tiles, small_tiles, cap, drop_off, perm, A);
   hipLaunchKernelGGL(permute_kernel, dim3(static_cast<unsigned>((A + 255) / 256)), dim3(256), 0, s,
                      idx, rank, blk, nblk, offsets, A, ly.k, ly.E, perm, inv, cap, drop_off);
   return hipGetLastError();
@@ -530,7 +606,7 @@ hipError_t launch_zero_counts_offsets(int32_t* counts, int32_t* offsets, int E, 
 hipError_t launch_build_tiles(const Layer& ly, const int32_t* offsets, const TileList& tiles,
                               const TileList& small_tiles, const TilePlan& plan, hipStream_t s) {
   hipLaunchKernelGGL(offsets_tiles_kernel, dim3(1), dim3(1024), 0, s, nullptr, offsets, nullptr,
-                     ly.E, plan, tiles, small_tiles, 0, nullptr, nullptr, int64_t(0));
+                     ly.E, with_tail(ly, plan), tiles, small_tiles, 0, nullptr, nullptr, int64_t(0));
   return hipGetLastError();
 }
 

@@ -1120,6 +1120,13 @@ hipError_t launch_shape(const GemmCall& c, hipStream_t s, int wg_per_cu) {
 
 int gemm_bf16_tile_m(int variant) { return variant == 0 ? ShapeLarge::BM : ShapeSmall::BM; }
 
+int gemm_bf16_round_tiles() {
+  const int64_t g = static_cast<int64_t>(device_cu_count()) * ShapeLarge::WG_PER_CU;
+  return static_cast<int>(((g + kXcds - 1) / kXcds) * kXcds);  // whole XCD rounds, as launched
+}
+
+int gemm_bf16_swiglu_tile_cols() { return ShapeLarge::BN / 2; }
+
 int gemm_bf16_planes_tile_n() { return ShapeRouter::BN; }
 
 hipError_t launch_gemm_bf16_planes_f32(const GemmCall& c, hipStream_t s) {
