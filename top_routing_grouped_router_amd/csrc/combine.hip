@@ -18,6 +18,14 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Expert-output rows are read once: loaded past the caches' retention (non-temporal), so the
+// layer's other operands keep their place in L2 and the last-level cache.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_once(const void* p) {
+  const u32x4v q = __builtin_nontemporal_load(static_cast<const u32x4v*>(p));
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
 constexpr int kMaxChunks = 8;  // per thread: K <= 256 * 8 * (16 / sizeof(T))
 
 template <typename T>
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int ci = threadIdx.x + c * nt;
-        if (j0 + u < k && ci < nch) raw[u][c] = *reinterpret_cast<const uint4*>(yr + ci * V);
+        if (j0 + u < k && ci < nch) raw[u][c] = load_once(yr + ci * V);
       }
     }
 #pragma unroll
