@@ -454,15 +454,13 @@ hipError_t run_experts(const Layer& ly, const void* z, const int32_t* perm, cons
 // ------------------------------------------------------------------ backward of the experts
 
 // Workspace of moe_experts_backward: the M-tile lists of the input-gradient GEMMs, dY and z in
-// sorted order (the dY buffer later holds the per-assignment input gradients), dH, and one
-// row of zeros read by the weight-gradient GEMMs past a group's last row.
+// sorted order (the dY buffer later holds the per-assignment input gradients), dH, the two
+// weight-gradient tile counters and the weight-gradient group order.
 struct BwdLayout {
-  size_t tcount, texpert, trow0, trows, scount, sexpert, srow0, srows, dy, zs, dh, zero, order, total;
+  size_t tcount, texpert, trow0, trows, scount, sexpert, srow0, srows, dy, zs, dh, counters, order, total;
   int32_t tile_cap, small_cap;
 };
-// the zero row, then the two weight-gradient tile counters (cleared together)
-constexpr size_t kZeroRowBytes = 512;
-constexpr size_t kZeroRegionBytes = kZeroRowBytes + 16;
+constexpr size_t kCounterBytes = 16;  // the two weight-gradient tile counters (cleared together)
 
 BwdLayout bwd_layout(const Layer& ly) {
   BwdLayout b{};
@@ -485,7 +483,7 @@ BwdLayout bwd_layout(const Layer& ly) {
   b.dy = c.take(A * static_cast<size_t>(ly.K) * es);
   b.zs = c.take(A * static_cast<size_t>(ly.K) * es);
   b.dh = c.take(A * 2 * static_cast<size_t>(ly.h) * es);
-  b.zero = c.take(kZeroRegionBytes);
+  b.counters = c.take(kCounterBytes);
   b.order = c.take(E * 4);
   b.total = c.off;
   return b;
@@ -522,8 +520,8 @@ hipError_t run_experts_backward(const Layer& ly, const moe_weights_t* w, const B
   hipError_t e;
   const int32_t* kept = a.offsets + ly.E;
   if ((e = launch_build_tiles(ly, a.offsets, tiles, small_tiles, plan, s)) != hipSuccess) return e;
-  if ((e = launch_fill_zero(at<void>(ws, L.zero), kZeroRegionBytes, s)) != hipSuccess) return e;
-  int32_t* counters = reinterpret_cast<int32_t*>(at<unsigned char>(ws, L.zero) + kZeroRowBytes);
+  if ((e = launch_fill_zero(at<void>(ws, L.counters), kCounterBytes, s)) != hipSuccess) return e;
+  int32_t* counters = at<int32_t>(ws, L.counters);
   int32_t* order = at<int32_t>(ws, L.order);
   if (ly.bf16 && (e = launch_expert_order(a.offsets, ly.E, order, s)) != hipSuccess) return e;
   if ((e = launch_gather_rows(a.dy_assign, A, a.perm, 1, kept, A, ly.K * es, dy_sorted, s)) != hipSuccess) return e;
@@ -561,7 +559,6 @@ hipError_t run_experts_backward(const Layer& ly, const moe_weights_t* w, const B
   g2.group_offsets = a.offsets;
   g2.groups = ly.E;
   g2.c_group_stride = ly.K * ly.h;
-  g2.zero_row = at<void>(ws, L.zero);
   g2.group_order = order;
   g2.tile_counter = counters;
   g2.a_rows = A;
@@ -598,7 +595,6 @@ hipError_t run_experts_backward(const Layer& ly, const moe_weights_t* w, const B
   g1.group_offsets = a.offsets;
   g1.groups = ly.E;
   g1.c_group_stride = 2 * ly.h * ly.K;
-  g1.zero_row = at<void>(ws, L.zero);
   g1.group_order = order;
   g1.tile_counter = counters + 1;
   g1.a_rows = A;

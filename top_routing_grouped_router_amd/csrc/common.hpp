@@ -268,12 +268,10 @@ struct GemmCall {
   // Weight-gradient mode (group_offsets != NULL): for each of `groups` groups g the product
   // C_g (dense_M, N) = sum over the contraction rows p in [group_offsets[g],
   // group_offsets[g + 1]) of A(., p) B(., p)^T, A and B both contraction-major (trans = 3);
-  // C_g starts c_group_stride elements after C_{g-1}. Rows past a group's end read zero_row
-  // (at least 512 zero bytes) instead.
+  // C_g starts c_group_stride elements after C_{g-1}. Rows past a group's end read as zeros.
   const int32_t* group_offsets;
   int32_t groups;
   int64_t c_group_stride;
-  const void* zero_row;
   // ... whose tiles are handed out in the order of group_order (groups by decreasing row count;
   // NULL = 0..groups-1) through tile_counter, one int32 that must be 0 at launch.
   const int32_t* group_order;

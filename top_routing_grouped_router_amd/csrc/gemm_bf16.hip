@@ -525,24 +525,42 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmCall& c, unsigned char*
     setup_fetched(f, t);
   };
 
-  // Row-major operands load through buffer descriptors (buffer_load ... lds): the k-stage step
-  // is a scalar offset, so a stage's loads need no per-lane address arithmetic. Contraction-major
-  // and weight-gradient operands (whose rows past a group's end come from a separate zero row)
-  // load through global addresses.
-  constexpr bool BUF = !TA && !TB && !WGRAD;
+  // Every operand loads through buffer descriptors (buffer_load ... lds) with uniform bases, so
+  // a stage's loads need no per-lane address arithmetic. Row-major operands and contraction-major
+  // weights: one descriptor per operand and tile, the k-stage step a scalar offset. Weight-
+  // gradient operands (contraction over a group's rows): the descriptor moves to the stage's first
+  // contraction row and its range ends at the group's last row, so rows past the group read as
+  // zeros (an out-of-range buffer load returns zero; the range check covers the per-lane offset,
+  // which therefore carries no k-stage step).
   // DMA loads of k-stage kt of tile t into ring slot `st` (lds0 or lds1).
   auto issue = [&](const TileState& t, int kt, unsigned char* st) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    // The descriptors' bases are uniform; readfirstlane keeps them in scalar registers. No
-    // range limit (every offset is below 4 GiB): row indices are clamped where they are made.
-    auto rsrc = [](const unsigned char* p) {
+    // bases and ranges are uniform; readfirstlane keeps them in scalar registers
+    auto rsrc = [](const unsigned char* p, uint32_t bytes) {
       const uint64_t v = reinterpret_cast<uint64_t>(p);
       const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
       const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+      const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
       return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
-                                               static_cast<short>(0), -1, 0x00020000);
+                                               static_cast<short>(0), static_cast<int>(n), 0x00020000);
     };
-    const __amdgpu_buffer_rsrc_t ra = rsrc(Ab), rb = rsrc(t.Bexp);
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t soa, sob;
+    if constexpr (WGRAD) {
+      const uint32_t da = static_cast<uint32_t>(kt) * a_step, db = static_cast<uint32_t>(kt) * b_step;
+      const int64_t la = static_cast<int64_t>(t.kcnt) * c.lda * 2 - da;
+      const int64_t lb = static_cast<int64_t>(t.kcnt) * c.ldb * 2 - db;
+      ra = rsrc(t.Abase + da, la > 0 ? static_cast<uint32_t>(la) : 0u);
+      rb = rsrc(t.Bexp + db, lb > 0 ? static_cast<uint32_t>(lb) : 0u);
+      soa = 0;
+      sob = 0;
+    } else {
+      // no range limit (every offset is below 4 GiB): row indices are clamped where they are made
+      ra = rsrc(Ab, 0xFFFFFFFFu);
+      rb = rsrc(t.Bexp, 0xFFFFFFFFu);
+      soa = static_cast<uint32_t>(kt) * a_step;
+      sob = static_cast<uint32_t>(kt) * b_step;
+    }
 #endif
 #pragma unroll
     for (int q = 0; q < S::NQ; ++q) {
@@ -553,22 +571,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmCall& c, unsigned char*
       // stored, so their loads are skipped (whatever LDS holds there only feeds output rows
       // that are dropped). The large tiles keep every load: the extra live register spills.
       if (S::BM < 256 && !TA && !WGRAD && is_a && i * S::kRowsPerDma >= t.rows) continue;
-      if constexpr (BUF) {
 #if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, LDS_PTR(st + i * 1024), 16, t.src_off[q],
-                                                 static_cast<uint32_t>(kt) * (is_a ? a_step : b_step), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, LDS_PTR(st + i * 1024), 16, t.src_off[q],
+                                               is_a ? soa : sob, 0, 0);
 #endif
-        continue;
-      }
-      const unsigned char* g = (is_a ? (WGRAD ? t.Abase : Ab) : t.Bexp) +
-                               (t.src_off[q] + static_cast<uint32_t>(kt) * (is_a ? a_step : b_step));
-      if (WGRAD) {
-        // contraction rows past the group's end read zeros
-        const int il = is_a ? i : i - S::BM / S::kRowsPerDma;
-        if (kt * S::BK + 2 * il + (lane >> 5) >= t.kcnt)
-          g = static_cast<const unsigned char*>(c.zero_row) + (lane & 31) * 16;
-      }
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), LDS_PTR(st + i * 1024), 16, 0, 0);
     }
     if constexpr (S::SCG == 1) {
       if (wave < S::NSC)
@@ -1208,7 +1214,7 @@ hipError_t launch_gemm_bf16_dgrad(const GemmCall& c, int variant, hipStream_t s)
 
 hipError_t launch_gemm_bf16_wgrad(const GemmCall& c, hipStream_t s) {
   using S = ShapeLarge;
-  if (c.trans != 3 || !c.group_offsets || !c.zero_row || !c.tile_counter || c.gather || c.scatter || c.bwd_h > 0 ||
+  if (c.trans != 3 || !c.group_offsets || !c.tile_counter || c.gather || c.scatter || c.bwd_h > 0 ||
       c.swiglu_h > 0 ||
       c.dense_M <= 0 || c.groups <= 0 || c.N <= 0 || c.N % 8 != 0 || c.dense_M % 8 != 0)
     return hipErrorInvalidValue;
