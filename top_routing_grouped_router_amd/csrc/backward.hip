@@ -84,13 +84,26 @@ __global__ __launch_bounds__(256) void sum_copies_kernel(const T* __restrict__ i
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int64_t t = i / cpr, c = i - t * cpr;
-    float acc[N], v[N];
+    float acc[N];
 #pragma unroll
     for (int e = 0; e < N; ++e) acc[e] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      Chunk<T>::load(in + (t * k + j) * width + c * N, v);
+    // the token's copies (read once: non-temporal) in batches of 8 whose loads are all issued
+    // before any is added
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4 raw[8];
 #pragma unroll
-      for (int e = 0; e < N; ++e) acc[e] += v[e];
+      for (int u = 0; u < 8; ++u) {
+        const T* p = in + (t * k + min(j0 + u, k - 1)) * width + c * N;
+        raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= k) break;
+        float v[N];
+        Chunk<T>::load(reinterpret_cast<const T*>(&raw[u]), v);
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[e] += v[e];
+      }
     }
     Chunk<T>::store(out + t * width + c * N, acc);
   }
