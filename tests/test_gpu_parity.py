@@ -260,20 +260,24 @@ def test_experts_forward(case):
 # Expert row counts whose main tile list (256-row M-tiles, hidden 128: one up/gate tile per
 # M-tile) is 260 M-tiles: one whole round of a 256-workgroup grid and a last round of 4 tiles,
 # which the dispatch moves to the remainder list (64-row tiles) from one expert -- the one with
-# a remainder already; none has one; none has one and the chosen expert's last M-tile is partial.
+# a remainder already; none has one; none has one and the chosen expert's last M-tile is partial;
+# no expert has 4 M-tiles to give, so nothing moves.
 TAIL_COUNTS = [
     [70 * 256, 70 * 256, 70 * 256, 50 * 256 + 40],
     [130 * 256, 130 * 256],
     [70 * 256 + 200, 70 * 256, 70 * 256, 49 * 256],
+    [3 * 256] * 86 + [2 * 256],
 ]
 
 
 def _tail_move(counts, round_tiles, ntn=1, bm=256, small_max=128):
-    """M-tiles the dispatch's thin-last-round rule moves for these counts (0: none)."""
+    """M-tiles the dispatch's thin-last-round rule moves for these counts (0: none, also when no
+    expert has that many)."""
     nb = [c // bm + (1 if c % bm > small_max else 0) for c in counts]
     work = sum(nb) * ntn
     tail = work % round_tiles
-    return -(-tail // ntn) if work > round_tiles and 0 < tail and 8 * tail <= round_tiles else 0
+    m = -(-tail // ntn) if work > round_tiles and 0 < tail and 8 * tail <= round_tiles else 0
+    return m if max(nb) >= m else 0
 
 
 @pytest.mark.parametrize("counts", TAIL_COUNTS, ids=lambda c: f"E{len(c)}-{sum(c)}")
