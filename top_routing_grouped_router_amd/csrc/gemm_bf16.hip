@@ -30,10 +30,13 @@
 //     panels through the last-level cache as well. Small tiles use only as many workgroups of
 //     an XCD as finish its chunk in the same number of rounds, so no round runs part-empty.
 //   * Operands reach LDS by DMA (16 bytes per lane, no register round trip); each 64-k stage
-//     is one whole 128-byte line per staged row. Row-major operands use buffer_load ... lds
-//     through a buffer descriptor per operand, the k-stage step a scalar offset; measured on
-//     the same box, that streams faster than global_load_lds (a 32768 x 4096 x 4096 dense
+//     is one whole 128-byte line per staged row. Every operand loads with buffer_load ... lds:
+//     row-major operands and contraction-major weights through one descriptor per operand,
+//     the k-stage step a scalar offset; the weight gradients' operands through a descriptor per
+//     stage whose range ends at the group's last row, so rows past it read as zeros. Measured
+//     on the same box, that streams faster than global_load_lds (a 32768 x 4096 x 4096 dense
 //     product 1191 -> 1248 TFLOP/s), and the operand loads need no per-lane 64-bit addresses.
+//     (The MXFP8 scale rows keep global_load_lds: descriptors measured within noise there.)
 //   * Staggered load issue (large tiles, weight-gradient tiles): of the two wavefronts sharing a
 //     SIMD, one issues its share of the next stage's loads before its first fragment reads, the
 //     other after its first k16 step, so the pair does not stall together on a full address
